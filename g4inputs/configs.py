@@ -1,0 +1,69 @@
+"""The five attention workloads, shaped like the Gemma 4 variants.
+
+Head counts, head widths and windows come from the variant tables
+[gemma4-pt-claude README, "Supported Models"; Gemma 4 Keras docs,
+``Gemma4Model`` table; vinija.ai Gemma 4 primer, "Window sizes by model
+family"]:
+
+* E2B: 8 query heads, 1 KV head, window 512, head_dim 256 / global 512.
+* 31B: 32 query heads, 16 KV heads on sliding layers and 4 on global ones,
+  window 1024, head_dim 256 / global 512, K=V on global layers.
+
+RoPE: theta 1e4 with every pair rotated on sliding layers; theta 1e6 with a
+quarter of the head rotated (zero-padded frequencies) on global layers.
+Scale ``1/sqrt(head_dim)`` everywhere.
+"""
+
+from dataclasses import dataclass
+import math
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    cfg_id: int            # seed component
+    kind: str              # "prefill" | "decode"
+    B: int
+    S: int                 # prefill sequence length (decode: 1)
+    Hq: int
+    Hkv: int
+    D: int
+    window: int            # 0 = global (causal)
+    rotary_dims: int
+    theta: float
+    k_eq_v: bool
+    len_lo: int = 0        # decode: cache lengths drawn from [len_lo, len_hi]
+    len_hi: int = 0
+
+    @property
+    def scale(self):
+        return 1.0 / math.sqrt(self.D)
+
+    @property
+    def cache_cap(self):
+        # Room for the longest cache plus the new token's own slot.
+        return self.len_hi + 1
+
+
+WORKLOADS = {
+    "e2b_sliding_prefill": Workload(
+        "e2b_sliding_prefill", 1, "prefill", B=1, S=1024, Hq=8, Hkv=1, D=256,
+        window=512, rotary_dims=256, theta=1e4, k_eq_v=False),
+    "e2b_global_prefill": Workload(
+        "e2b_global_prefill", 2, "prefill", B=1, S=8192, Hq=8, Hkv=1, D=512,
+        window=0, rotary_dims=128, theta=1e6, k_eq_v=False),
+    "31b_sliding_prefill": Workload(
+        "31b_sliding_prefill", 3, "prefill", B=2, S=16384, Hq=32, Hkv=16, D=256,
+        window=1024, rotary_dims=256, theta=1e4, k_eq_v=False),
+    "31b_global_kv_prefill": Workload(
+        "31b_global_kv_prefill", 4, "prefill", B=1, S=32768, Hq=32, Hkv=4, D=512,
+        window=0, rotary_dims=128, theta=1e6, k_eq_v=True),
+    "31b_global_kv_decode": Workload(
+        "31b_global_kv_decode", 5, "decode", B=32, S=1, Hq=32, Hkv=4, D=512,
+        window=0, rotary_dims=128, theta=1e6, k_eq_v=True,
+        len_lo=32768, len_hi=131072),
+}
+
+
+def get(name):
+    return WORKLOADS[name]

@@ -1,0 +1,218 @@
+"""fp64 oracle for causal / sliding-window GQA softmax attention.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Sources
+-------
+* Scaled dot-product softmax attention: weights are the softmax over keys of
+  ``q_i . k_j`` times a scale, and the output is the weighted sum of values
+  [vinija.ai Gemma 4 primer, "Why long context is difficult" (attention
+  equation) and "Sliding-window attention" (alpha_ij equation)].  The scale
+  is an argument: the primer uses ``1/sqrt(d_k)``, while the PyTorch port
+  says QK-norm replaces that factor [gemma4-pt-claude README, "Key
+  architectural features"].
+* Sliding-window (local) layers: token ``i`` attends only to keys in a
+  window of size ``w`` ending at ``i`` [vinija.ai Gemma 4 primer, "Local
+  attention" and "Sliding-window attention", window equations]; windows are
+  512 on E2B/E4B and 1024 on 31B/26B ["Window sizes by model family"].
+* Global layers: every earlier key is visible, and the layer stays causal
+  [vinija.ai Gemma 4 primer, "Global attention layers"; Gemma 4 Keras docs,
+  "What changed from Gemma 3" (global layers stay causal)].
+* GQA: several query heads share one key/value head [Gemma 4 Keras docs,
+  ``Gemma4Model`` table, ``num_kv_heads``; gemma4-pt-claude README,
+  "Supported Models"].
+* Decode over a KV cache: the new query attends over the stored keys and
+  values of every earlier token [vinija.ai Gemma 4 primer, "KV cache and
+  long-context scaling"; gemma4-pt-claude README, "KV Cache"].
+
+Readings where the pages are silent or disagree
+-----------------------------------------------
+* Window boundary: key ``j`` is visible from row ``i`` iff ``0 <= i - j < w``
+  (``w`` keys including the token itself).  The primer's sum runs from
+  ``i - w`` (``w + 1`` keys); the PyTorch port keeps ``w`` cache slots per
+  sliding layer, which fits ``w`` keys.  ``w = 0`` means global (``j <= i``).
+* GQA grouping is contiguous: query head ``h`` uses KV head
+  ``h // (Hq // Hkv)``.
+* LSE is the natural log of the softmax denominator, ``log sum_j exp(s_ij)``.
+* A row with no visible key (never produced by these masks) outputs zeros
+  and ``lse = -inf``.
+* Decode: the cache holds post-prologue keys and values; the query attends
+  over the first ``n_b`` rows of its sequence's cache (``n_b`` includes the
+  new token's own slot).
+
+Pins (tests/test_oracle_attention.py)
+-------------------------------------
+* The band oracle against the brute-force explicit-mask oracle on tiny
+  shapes across window, GQA and length edges (brute force);
+* both against ``torch.nn.functional.scaled_dot_product_attention`` in
+  float64 with a mask built from ``torch.tril`` (a library routine), GQA via
+  repeated KV heads;
+* closed forms: softmax rows sum to 1; visible-key count ``min(i+1, w)``;
+  ``w = 1`` gives ``out = v``; ``S <= w`` equals the global result; a
+  scale of 0 gives ``lse = log(count)``; decode of the last row equals the
+  prefill row.
+"""
+
+import numpy as np
+
+
+def visible(i, j, window):
+    """Mask predicate: may query row ``i`` see key ``j``?
+
+    Global (``window == 0``): ``j <= i``.  Sliding: ``0 <= i - j < window``.
+    """
+    d = i - j
+    if window == 0:
+        return d >= 0
+    return (d >= 0) & (d < window)
+
+
+def mask_bruteforce(S, window):
+    """Explicit ``S x S`` boolean mask built element by element."""
+    m = np.zeros((S, S), dtype=bool)
+    for i in range(S):
+        for j in range(S):
+            m[i, j] = bool(visible(i, j, window))
+    return m
+
+
+def _kv_head(h, Hq, Hkv):
+    return h // (Hq // Hkv)
+
+
+def attention_bruteforce(q, k, v, scale, window):
+    """Brute-force attention over the full ``S x S`` logit matrix.
+
+    ``q``: ``[B, S, Hq, D]``; ``k``, ``v``: ``[B, S, Hkv, D]`` (any real
+    dtype, widened to fp64).  Returns ``(out [B,S,Hq,D], lse [B,Hq,S],
+    weights [B,Hq,S,S])``.  For tiny shapes only.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    mask = mask_bruteforce(S, window)
+    out = np.zeros((B, S, Hq, D))
+    lse = np.full((B, Hq, S), -np.inf)
+    weights = np.zeros((B, Hq, S, S))
+    for b in range(B):
+        for h in range(Hq):
+            g = _kv_head(h, Hq, Hkv)
+            s = scale * (q[b, :, h, :] @ k[b, :, g, :].T)
+            s = np.where(mask, s, -np.inf)
+            for i in range(S):
+                if not mask[i].any():
+                    continue
+                mx = np.max(s[i])
+                e = np.exp(s[i] - mx)
+                den = np.sum(e)
+                weights[b, h, i] = e / den
+                lse[b, h, i] = mx + np.log(den)
+            out[b, :, h, :] = weights[b, h] @ v[b, :, g, :]
+    return out, lse, weights
+
+
+def _band_rows(q_rows, k_band, v_band, rows, key0, scale, window):
+    """Softmax attention of the given query rows over one key band."""
+    s = scale * (q_rows @ k_band.T)                       # [nr, nk]
+    keys = key0 + np.arange(k_band.shape[0])
+    m = visible(rows[:, None], keys[None, :], window)
+    s = np.where(m, s, -np.inf)
+    has = m.any(axis=1)
+    mx = np.where(has, np.max(s, axis=1), 0.0)
+    e = np.where(m, np.exp(s - mx[:, None]), 0.0)
+    den = e.sum(axis=1)
+    safe = np.where(has, den, 1.0)
+    o = (e @ v_band) / safe[:, None]
+    o[~has] = 0.0
+    lse = np.where(has, mx + np.log(safe), -np.inf)
+    return o, lse
+
+
+def attention_band(q, k, v, scale, window, rows=None, block=256):
+    """Row-blocked attention that only touches keys inside each row's band.
+
+    Same contract as :func:`attention_bruteforce` minus the weights.  If
+    ``rows`` (a sorted 1-D array of query rows) is given, only those rows are
+    computed and the results have ``len(rows)`` in place of ``S``:
+    ``out [B, R, Hq, D]``, ``lse [B, Hq, R]``.
+    """
+    q = np.asarray(q)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = rows.shape[0]
+    out = np.zeros((B, R, Hq, D))
+    lse = np.full((B, Hq, R), -np.inf)
+    for b in range(B):
+        for g in range(Hkv):
+            heads = [h for h in range(Hq) if _kv_head(h, Hq, Hkv) == g]
+            for r0 in range(0, R, block):
+                rr = rows[r0:r0 + block]
+                hi = int(rr[-1]) + 1
+                lo = 0 if window == 0 else max(0, int(rr[0]) - window + 1)
+                kb = np.asarray(k[b, lo:hi, g, :], np.float64)
+                vb = np.asarray(v[b, lo:hi, g, :], np.float64)
+                for h in heads:
+                    qr = np.asarray(q[b, rr, h, :], np.float64)
+                    o, l_ = _band_rows(qr, kb, vb, rr, lo, scale, window)
+                    out[b, r0:r0 + block, h, :] = o
+                    lse[b, h, r0:r0 + block] = l_
+    return out, lse
+
+
+def decode_attention(q, k_cache, v_cache, n, scale, heads=None, batch=None):
+    """Single-token decode: query ``q[b, h]`` over cache rows ``[0, n[b])``.
+
+    ``q``: ``[B, Hq, D]`` (post-prologue); ``k_cache``, ``v_cache``:
+    ``[B, Hkv, cap, D]`` (``v_cache`` may be the same array as ``k_cache``);
+    ``n``: ``[B]`` visible lengths.  ``batch`` / ``heads`` restrict the work
+    to a subset (results are indexed ``[len(batch), len(heads)]``).
+    Returns ``(out [B', H', D], lse [B', H'])``.
+    """
+    Bq, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    batch = list(range(Bq)) if batch is None else list(batch)
+    heads = list(range(Hq)) if heads is None else list(heads)
+    out = np.zeros((len(batch), len(heads), D))
+    lse = np.full((len(batch), len(heads)), -np.inf)
+    for bi, b in enumerate(batch):
+        nb = int(n[b])
+        for hi, h in enumerate(heads):
+            g = _kv_head(h, Hq, Hkv)
+            if nb <= 0:
+                continue
+            kk = np.asarray(k_cache[b, g, :nb, :], np.float64)
+            vv = kk if v_cache is k_cache else np.asarray(v_cache[b, g, :nb, :], np.float64)
+            s = scale * (kk @ np.asarray(q[b, h], np.float64))
+            mx = np.max(s)
+            e = np.exp(s - mx)
+            den = np.sum(e)
+            out[bi, hi] = (e @ vv) / den
+            lse[bi, hi] = mx + np.log(den)
+    return out, lse
+
+
+def visible_count(S, window):
+    """Number of keys each prefill row sees, by enumeration of the mask."""
+    i = np.arange(S)[:, None]
+    j = np.arange(S)[None, :]
+    return visible(i, j, window).sum(axis=1)
+
+
+def visible_pairs(S, window):
+    """Total visible (row, key) pairs of one head, by the count per row."""
+    return int(visible_count(S, window).sum()) if S <= 4096 else _pairs_closed(S, window)
+
+
+def _pairs_closed(S, window):
+    # Counting rows of the mask in closed form: row i sees min(i+1, w) keys
+    # (all i+1 for a global layer).  Used for sizes whose S x S mask would
+    # not fit in memory; equality with the enumeration is tested.
+    if window == 0:
+        return S * (S + 1) // 2
+    w = window
+    if S <= w:
+        return S * (S + 1) // 2
+    return w * (w + 1) // 2 + (S - w) * w
