@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Benchmark of the Gemma 4 31B attention hot path on one MI355X.
+
+One step = one pass of every hot-path stage over the 31B-shaped workloads,
+inputs resident in HBM:
+
+  sliding prefill   B=2, S=16384, 32 q / 16 KV heads, D=256, window 1024:
+                    q/k/v prologue (RMSNorm + RoPE) + attention
+  global prefill    B=1, S=32768, 32 q / 4 KV heads, D=512, K=V tied:
+                    q prologue + attention (K=V pre-pass included)
+  global decode     B=32, one token each, KV lengths ~ U[32768, 131072],
+                    32 q / 4 KV heads, D=512, one cache tensor for K and V:
+                    q prologue at position = cache length + split-KV decode
+
+Prints one JSON line.  ``value`` is the prefill attention throughput
+(algorithmic flops = 4*D per visible (row, key) pair per query head, over
+both prefill calls); the decode stream rate, per-stage timings, the roofline
+of the dominant kernel and the CPU oracle baseline are in the same line.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["sliding", "global", "decode"], default=None,
+                    help="time one stage only (profiling aid)")
+    return ap.parse_args()
+
+
+class Stage:
+    def __init__(self, name):
+        self.name = name
+        self.ms = []
+
+
+def build_workloads(torch, g4, gen, W):
+    dev = "cuda"
+    st = {}
+
+    # ---- 31B sliding prefill
+    c = W["31b_sliding_prefill"]
+    q_raw = gen.normal_bf16((c.B, c.S, c.Hq, c.D), gen.seed_key(c.cfg_id, gen.Q), dev)
+    k_raw = gen.normal_bf16((c.B, c.S, c.Hkv, c.D), gen.seed_key(c.cfg_id, gen.K), dev)
+    v_raw = gen.normal_bf16((c.B, c.S, c.Hkv, c.D), gen.seed_key(c.cfg_id, gen.V), dev)
+    wq = gen.norm_weight(c.D, gen.seed_key(c.cfg_id, gen.WQ)).to(dev)
+    wk = gen.norm_weight(c.D, gen.seed_key(c.cfg_id, gen.WK)).to(dev)
+    desc = g4.layer_desc(c.Hq, c.Hkv, c.D, window=c.window, rotary_dims=c.rotary_dims, rope_theta=c.theta)
+    st["sliding"] = dict(c=c, desc=desc, q_raw=q_raw, k_raw=k_raw, v_raw=v_raw, wq=wq, wk=wk,
+                         q=torch.empty_like(q_raw), k=torch.empty_like(k_raw), v=torch.empty_like(v_raw),
+                         out=torch.empty_like(q_raw))
+
+    # ---- 31B global prefill, K=V
+    c = W["31b_global_kv_prefill"]
+    q_raw = gen.normal_bf16((c.B, c.S, c.Hq, c.D), gen.seed_key(c.cfg_id, gen.Q), dev)
+    X = gen.normal_bf16((c.B, c.S, c.Hkv, c.D), gen.seed_key(c.cfg_id, gen.X), dev)
+    wq = gen.norm_weight(c.D, gen.seed_key(c.cfg_id, gen.WQ)).to(dev)
+    wk = gen.norm_weight(c.D, gen.seed_key(c.cfg_id, gen.WK)).to(dev)
+    desc = g4.layer_desc(c.Hq, c.Hkv, c.D, window=0, k_eq_v=True, rotary_dims=c.rotary_dims,
+                         rope_theta=c.theta)
+    ws = torch.empty(g4.g4attn_prefill_workspace_bytes(desc, c.B, c.S), dtype=torch.uint8, device=dev)
+    st["global"] = dict(c=c, desc=desc, q_raw=q_raw, X=X, wq=wq, wk=wk, q=torch.empty_like(q_raw),
+                        out=torch.empty_like(q_raw), ws=ws)
+
+    # ---- 31B global decode, K=V cache
+    c = W["31b_global_kv_decode"]
+    L = gen.decode_lengths(c.B, c.len_lo, c.len_hi, gen.seed_key(c.cfg_id, gen.LENS))
+    n = L.astype(np.int64) + 1            # the new token's own row is slot L_b
+    cap = c.cache_cap
+    cache = torch.empty((c.B, c.Hkv, cap, c.D), dtype=torch.bfloat16, device=dev)
+    for b in range(c.B):
+        cache[b, :, :n[b]] = gen.normal_bf16((c.Hkv, int(n[b]), c.D), gen.seed_key(c.cfg_id, gen.CACHE, b), dev)
+    q_raw = gen.normal_bf16((c.B, 1, c.Hq, c.D), gen.seed_key(c.cfg_id, gen.QDEC), dev)
+    wq = gen.norm_weight(c.D, gen.seed_key(c.cfg_id, gen.WQ)).to(dev)
+    desc = g4.layer_desc(c.Hq, c.Hkv, c.D, window=0, rotary_dims=c.rotary_dims, rope_theta=c.theta)
+    pos0 = torch.from_numpy(L.astype(np.int32)).to(dev)
+    kv_len = torch.from_numpy(n.astype(np.int32)).to(dev)
+    max_len = int(n.max())
+    dws = torch.empty(g4.g4attn_decode_workspace_bytes(desc, c.B, max_len, 0), dtype=torch.uint8, device=dev)
+    st["decode"] = dict(c=c, desc=desc, cache=cache, q_raw=q_raw, wq=wq, pos0=pos0, kv_len=kv_len,
+                        max_len=max_len, max_pos=int(L.max()), n=n, q=torch.empty((c.B, 1, c.Hq, c.D),
+                        dtype=torch.bfloat16, device=dev), out=torch.empty((c.B, c.Hq, c.D),
+                        dtype=torch.bfloat16, device=dev), ws=dws)
+    torch.cuda.synchronize()
+    return st
+
+
+def run_sliding(g4, s):
+    c = s["c"]
+    g4.g4attn_norm_rope(s["q_raw"], s["q"], s["wq"], c.D, c.rotary_dims, c.theta)
+    g4.g4attn_norm_rope(s["k_raw"], s["k"], s["wk"], c.D, c.rotary_dims, c.theta)
+    g4.g4attn_norm_rope(s["v_raw"], s["v"], None, c.D, 0, c.theta)
+
+
+def run_sliding_attn(g4, s):
+    g4.g4attn_prefill(s["desc"], s["q"], s["k"], s["v"], s["out"])
+
+
+def run_global_pro(g4, s):
+    c = s["c"]
+    g4.g4attn_norm_rope(s["q_raw"], s["q"], s["wq"], c.D, c.rotary_dims, c.theta)
+
+
+def run_global_attn(g4, s):
+    g4.g4attn_prefill(s["desc"], s["q"], s["X"], None, s["out"], w_k=s["wk"], workspace=s["ws"])
+
+
+def run_decode_pro(g4, s):
+    c = s["c"]
+    g4.g4attn_norm_rope(s["q_raw"], s["q"], s["wq"], c.D, c.rotary_dims, c.theta, pos0=s["pos0"],
+                        max_pos=s["max_pos"])
+
+
+def run_decode_attn(g4, s):
+    g4.g4attn_decode(s["desc"], s["q"].view(s["q"].shape[0], s["q"].shape[2], s["q"].shape[3]),
+                     s["cache"], s["cache"], s["kv_len"], s["max_len"], s["out"], workspace=s["ws"])
+
+
+def cpu_baseline(torch, gen, st, budget_s=15.0):
+    """The fp64 oracle on a bounded sample of the K=V global prefill.
+
+    Sample: KV group 0 (8 query heads), the last R rows of the sequence (each
+    sees every earlier key), with R doubled until the run takes ~budget_s.
+    The rate counts the same algorithmic flops as the GPU (4*D per visible
+    pair per query head).
+    """
+    from oracle import attention as oat
+    from oracle import norm_rope as onr
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    s = st["global"]
+    c = s["c"]
+    G = c.Hq // c.Hkv
+    S = c.S
+    torch.cuda.synchronize()
+    X = gen.to_f64(s["X"][0, :, 0])                         # [S, D] raw tied projection, group 0
+    q = gen.to_f64(s["q"][0, :, :G])                        # [S, G, D] post-prologue queries
+    wk = gen.to_f64(s["wk"])
+    t0 = time.perf_counter()
+    K, V = onr.kv_tied_k_v(X[None, :, None, :], wk, np.arange(S)[None, :], c.rotary_dims, c.theta)
+    t_pro = time.perf_counter() - t0
+    R, done_pairs, elapsed = 16, 0, 0.0
+    while True:
+        rows = np.arange(S - R, S)
+        t0 = time.perf_counter()
+        oat.attention_band(q[None, :, :, :], K, V, c.scale, 0, rows=rows)
+        dt = time.perf_counter() - t0
+        pairs = int(((rows + 1).sum())) * G
+        if dt > budget_s / 3 or R >= 4096:
+            done_pairs, elapsed = pairs, dt
+            break
+        R *= 2
+    tflops = 4.0 * c.D * done_pairs / elapsed / 1e12
+    return {"value": tflops, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"31B K=V global prefill, KV group 0 ({G} q heads), last {R} rows x all "
+                      f"earlier keys ({done_pairs} visible pairs) in {elapsed:.2f}s; K/V prologue of "
+                      f"the group {t_pro:.2f}s not counted"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the attention path shards by KV head / batch without collectives).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import decoder_attention_g4attn_amd as g4
+    from g4inputs import WORKLOADS, gen
+
+    g4.load()
+    torch.cuda.set_device(0)
+    st = build_workloads(torch, g4, gen, WORKLOADS)
+
+    plan = [("sliding_prologue", run_sliding, "sliding"), ("sliding_attn", run_sliding_attn, "sliding"),
+            ("global_prologue", run_global_pro, "global"), ("global_attn", run_global_attn, "global"),
+            ("decode_prologue", run_decode_pro, "decode"), ("decode_attn", run_decode_attn, "decode")]
+    if args.only:
+        plan = [p for p in plan if p[2] == args.only]
+
+    def step(record):
+        evs = []
+        for name, fn, key in plan:
+            if record:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn(g4, st[key])
+                e1.record()
+                evs.append((name, e0, e1))
+            else:
+                fn(g4, st[key])
+        return evs
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    all_evs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        all_evs.append(step(True))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {}
+    for evs in all_evs:
+        for name, e0, e1 in evs:
+            ms.setdefault(name, []).append(e0.elapsed_time(e1))
+    avg = {k: float(np.mean(v)) for k, v in ms.items()}
+
+    cs, cg, cd = st["sliding"]["c"], st["global"]["c"], st["decode"]["c"]
+    fl_sliding = 4.0 * cs.D * g4.visible_pairs(cs.S, cs.window) * cs.Hq * cs.B
+    fl_global = 4.0 * cg.D * g4.visible_pairs(cg.S, 0) * cg.Hq * cg.B
+    dec = st["decode"]
+    dec_bytes = float(dec["n"].sum()) * cd.Hkv * cd.D * 2 + 2.0 * cd.B * cd.Hq * cd.D * 2
+    res = {}
+    if "sliding_attn" in avg:
+        res["sliding_prefill_tflops"] = fl_sliding / avg["sliding_attn"] / 1e9
+    if "global_attn" in avg:
+        res["global_prefill_tflops"] = fl_global / avg["global_attn"] / 1e9
+    if "decode_attn" in avg:
+        res["decode_GBps"] = dec_bytes / avg["decode_attn"] / 1e6
+    prefill_ms = avg.get("sliding_attn", 0.0) + avg.get("global_attn", 0.0)
+    prefill_fl = (fl_sliding if "sliding_attn" in avg else 0) + (fl_global if "global_attn" in avg else 0)
+    value = prefill_fl / prefill_ms / 1e9 if prefill_ms > 0 else None
+    ms_per_step = wall * 1e3 / args.steps
+
+    roof = None
+    if "global_attn" in avg:
+        ach = res["global_prefill_tflops"]
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "kernel": "g4attn_prefill on the 31B K=V global layer (K=V pre-pass + prefill_kernel<512,K=V>)",
+                "flops_per_launch": fl_global}
+    out = {
+        "metric": "prefill attention TFLOP/s (31B global/sliding) + decode KV GB/s, 1xMI355X",
+        "value": round(value, 3) if value else None,
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {
+            "workload": "Gemma 4 31B attention layers: sliding prefill B2 S16384 Hq32 Hkv16 D256 w1024; "
+                        "global K=V prefill B1 S32768 Hq32 Hkv4 D512; global K=V decode B32 "
+                        "L~U[32768,131072] Hq32 Hkv4 D512",
+            "value_is": "prefill attention TFLOP/s over the two 31B prefill calls",
+            "parallelism": "single GPU",
+        },
+        "decode_GBps": round(res.get("decode_GBps", 0.0), 1) if "decode_GBps" in res else None,
+        "decode_hbm_frac": round(res["decode_GBps"] / PEAK_HBM_GBPS, 4) if "decode_GBps" in res else None,
+        "sliding_prefill_tflops": round(res.get("sliding_prefill_tflops", 0.0), 2) if "sliding_prefill_tflops" in res else None,
+        "global_prefill_tflops": round(res.get("global_prefill_tflops", 0.0), 2) if "global_prefill_tflops" in res else None,
+        "stage_ms": {k: round(v, 4) for k, v in avg.items()},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline and "global_attn" in avg:
+        out["cpu_baseline"] = cpu_baseline(torch, gen, st)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

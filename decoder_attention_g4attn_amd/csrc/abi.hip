@@ -1,0 +1,223 @@
+// C ABI of libg4attn: argument validation and dispatch to the kernels.
+//
+// Every entry point checks all host-visible arguments before any HIP call
+// and returns a g4attn_status; on error nothing is launched.  Cache overflow
+// is an error rather than an eviction, as the PyTorch port's KV cache raises
+// when a write would overflow it [gemma4-pt-claude README, "KV Cache"].
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/g4attn.h"
+#include "g4attn_internal.h"
+
+namespace {
+
+thread_local int32_t t_last_hip_error = 0;
+
+constexpr int32_t kVersion = 100;  // 0.1.0
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool strides_ok(const int64_t* s) {
+  if (!s) return false;
+  for (int i = 0; i < 3; ++i)
+    if (s[i] < 0 || (s[i] & 7) != 0) return false;  // 16-byte rows
+  return true;
+}
+
+bool head_dim_ok(int32_t D) { return D == 256 || D == 512; }
+bool rot_ok(int32_t D, int32_t rot) { return rot == 0 || rot == D / 4 || rot == D; }
+
+g4attn_status desc_check(const g4attn_layer_desc* d) {
+  if (!d) return G4ATTN_ERR_NULL;
+  if (d->num_q_heads < 1 || d->num_kv_heads < 1 || d->num_q_heads % d->num_kv_heads != 0)
+    return G4ATTN_ERR_SHAPE;
+  if (d->num_kv_heads > 65535) return G4ATTN_ERR_SHAPE;
+  if (!head_dim_ok(d->head_dim)) return G4ATTN_ERR_UNSUPPORTED;
+  if (d->window < 0) return G4ATTN_ERR_SHAPE;
+  if (d->k_eq_v != 0 && d->k_eq_v != 1) return G4ATTN_ERR_SHAPE;
+  if (!rot_ok(d->head_dim, d->rotary_dims)) return G4ATTN_ERR_UNSUPPORTED;
+  if (!(d->rope_theta > 0.f) || !isfinite(d->rope_theta)) return G4ATTN_ERR_SHAPE;
+  if (!(d->rms_eps >= 0.f) || !isfinite(d->rms_eps)) return G4ATTN_ERR_SHAPE;
+  if (!isfinite(d->scale)) return G4ATTN_ERR_SHAPE;
+  return G4ATTN_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+g4attn_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return G4ATTN_OK;
+  t_last_hip_error = (int32_t)e;
+  return G4ATTN_ERR_HIP;
+}
+
+// Decode: rows per split chunk (a multiple of 64) and the split count.
+int64_t decode_chunk(const g4attn_layer_desc* d, int32_t B, int32_t max_kv_len, int32_t num_splits) {
+  int64_t target;
+  if (num_splits > 0) {
+    target = num_splits;
+  } else {  // aim for ~4096 workgroups over the whole batch
+    const int64_t groups = (int64_t)B * d->num_kv_heads;
+    target = (4096 + groups - 1) / groups;
+    if (target < 1) target = 1;
+  }
+  int64_t c = ((int64_t)max_kv_len + target - 1) / target;
+  c = (c + 63) / 64 * 64;
+  if (num_splits == 0 && c < 256) c = 256;
+  return c;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t g4attn_version(void) { return kVersion; }
+
+int32_t g4attn_last_hip_error(void) { return t_last_hip_error; }
+
+const char* g4attn_status_str(g4attn_status s) {
+  switch (s) {
+    case G4ATTN_OK: return "ok";
+    case G4ATTN_ERR_NULL: return "a required pointer is NULL";
+    case G4ATTN_ERR_SHAPE: return "sizes inconsistent or out of range";
+    case G4ATTN_ERR_LAYOUT: return "misaligned pointer or stride";
+    case G4ATTN_ERR_UNSUPPORTED: return "configuration not implemented";
+    case G4ATTN_ERR_CACHE_OVERFLOW: return "KV cache capacity exceeded";
+    case G4ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case G4ATTN_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+g4attn_status g4attn_norm_rope(const g4attn_bf16* x, g4attn_bf16* y, const g4attn_bf16* weight,
+                               int32_t B, int32_t S, int32_t H, int32_t head_dim,
+                               int32_t rotary_dims, float rope_theta, float rms_eps,
+                               const int64_t x_strides[3], const int64_t y_strides[3],
+                               const int32_t* pos0, int32_t max_pos, int32_t y_cache_cap,
+                               void* stream) {
+  if (!x || !y || !x_strides) return G4ATTN_ERR_NULL;
+  if (y_cache_cap == 0 && !y_strides) return G4ATTN_ERR_NULL;
+  if (B < 1 || S < 1 || H < 1 || B > 65535 || y_cache_cap < 0) return G4ATTN_ERR_SHAPE;
+  if (!head_dim_ok(head_dim) || !rot_ok(head_dim, rotary_dims)) return G4ATTN_ERR_UNSUPPORTED;
+  if (!(rope_theta > 0.f) || !isfinite(rope_theta) || !(rms_eps >= 0.f) || !isfinite(rms_eps))
+    return G4ATTN_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(y) || (weight && !aligned16(weight))) return G4ATTN_ERR_LAYOUT;
+  if (!strides_ok(x_strides) || (y_cache_cap == 0 && !strides_ok(y_strides))) return G4ATTN_ERR_LAYOUT;
+  const int64_t top = pos0 ? (int64_t)max_pos : (int64_t)S - 1;
+  if (pos0 && max_pos < S - 1) return G4ATTN_ERR_SHAPE;
+  if (y_cache_cap > 0 && top >= y_cache_cap) return G4ATTN_ERR_CACHE_OVERFLOW;
+
+  g4attn::NormRopeArgs a{};
+  a.x = x; a.y = y; a.w = weight;
+  a.B = B; a.S = S; a.H = H; a.D = head_dim; a.rot = rotary_dims;
+  a.log2_theta = log2((double)rope_theta);
+  a.eps = rms_eps;
+  for (int i = 0; i < 3; ++i) {
+    a.xs[i] = x_strides[i];
+    a.ys[i] = y_cache_cap > 0 ? 0 : y_strides[i];
+  }
+  a.pos0 = pos0;
+  a.cache_cap = y_cache_cap;
+  return hip_status(g4attn::launch_norm_rope(a, (hipStream_t)stream));
+}
+
+size_t g4attn_prefill_workspace_bytes(const g4attn_layer_desc* d, int32_t B, int32_t S) {
+  if (!d || B < 1 || S < 1 || d->num_kv_heads < 1 || !d->k_eq_v) return 0;
+  const size_t rows = (size_t)B * d->num_kv_heads * S;
+  return align256(rows * sizeof(float)) + align256(rows * 128 * sizeof(uint16_t));
+}
+
+g4attn_status g4attn_prefill(const g4attn_layer_desc* d, const g4attn_bf16* q,
+                             const g4attn_bf16* k, const g4attn_bf16* v, const g4attn_bf16* w_k,
+                             g4attn_bf16* out, float* lse, int32_t B, int32_t S,
+                             const int64_t q_strides[3], const int64_t kv_strides[3],
+                             const int64_t o_strides[3], void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  g4attn_status st = desc_check(d);
+  if (st != G4ATTN_OK) return st;
+  if (!q || !k || !out || !q_strides || !kv_strides || !o_strides) return G4ATTN_ERR_NULL;
+  if (d->k_eq_v) {
+    if (!w_k) return G4ATTN_ERR_NULL;
+    if (v) return G4ATTN_ERR_SHAPE;  // K=V takes one tensor
+    if (d->head_dim != 512 || d->rotary_dims != 128) return G4ATTN_ERR_UNSUPPORTED;
+  } else if (!v) {
+    return G4ATTN_ERR_NULL;
+  }
+  if (B < 1 || S < 1 || B > 65535) return G4ATTN_ERR_SHAPE;
+  if ((int64_t)S * (d->num_q_heads / d->num_kv_heads) > (int64_t)INT32_MAX) return G4ATTN_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || (v && !aligned16(v)) || (w_k && !aligned16(w_k)) ||
+      !aligned16(out) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return G4ATTN_ERR_LAYOUT;
+  if (!strides_ok(q_strides) || !strides_ok(kv_strides) || !strides_ok(o_strides)) return G4ATTN_ERR_LAYOUT;
+  const size_t need = g4attn_prefill_workspace_bytes(d, B, S);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return G4ATTN_ERR_WORKSPACE;
+
+  g4attn::PrefillArgs a{};
+  a.q = q; a.k = k; a.v = v; a.w_k = w_k; a.out = out; a.lse = lse;
+  a.B = B; a.S = S; a.Hq = d->num_q_heads; a.Hkv = d->num_kv_heads; a.D = d->head_dim;
+  a.window = d->window; a.kv_tied = d->k_eq_v;
+  a.scale_log2 = d->scale * g4attn::kLog2e;
+  for (int i = 0; i < 3; ++i) { a.qs[i] = q_strides[i]; a.ks[i] = kv_strides[i]; a.os[i] = o_strides[i]; }
+  hipStream_t s = (hipStream_t)stream;
+  if (d->k_eq_v) {
+    const size_t rows = (size_t)B * d->num_kv_heads * S;
+    float* r = (float*)workspace;
+    uint16_t* krot = (uint16_t*)((char*)workspace + align256(rows * sizeof(float)));
+    g4attn::KvPrepArgs p{};
+    p.x = k; p.w_k = w_k; p.r = r; p.krot = krot;
+    p.B = B; p.S = S; p.Hkv = d->num_kv_heads; p.rot = d->rotary_dims;
+    p.log2_theta = log2((double)d->rope_theta);
+    p.eps = d->rms_eps;
+    for (int i = 0; i < 3; ++i) p.xs[i] = kv_strides[i];
+    st = hip_status(g4attn::launch_kv_prep(p, s));
+    if (st != G4ATTN_OK) return st;
+    a.r = r; a.krot = krot;
+  }
+  return hip_status(g4attn::launch_prefill(a, s));
+}
+
+size_t g4attn_decode_workspace_bytes(const g4attn_layer_desc* d, int32_t B, int32_t max_kv_len,
+                                     int32_t num_splits) {
+  if (!d || B < 1 || max_kv_len < 1 || num_splits < 0 || d->num_kv_heads < 1 || d->num_q_heads < 1 ||
+      !head_dim_ok(d->head_dim))
+    return 0;
+  const int64_t c = decode_chunk(d, B, max_kv_len, num_splits);
+  const int64_t ns = ((int64_t)max_kv_len + c - 1) / c;
+  const size_t ph = (size_t)B * d->num_q_heads;
+  return align256(ph * ns * d->head_dim * sizeof(float)) + align256(ph * ns * sizeof(float));
+}
+
+g4attn_status g4attn_decode(const g4attn_layer_desc* d, const g4attn_bf16* q,
+                            const g4attn_bf16* k_cache, const g4attn_bf16* v_cache,
+                            const int32_t* kv_len, int32_t B, int32_t max_kv_len,
+                            int32_t cache_cap, g4attn_bf16* out, float* lse, int32_t num_splits,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  g4attn_status st = desc_check(d);
+  if (st != G4ATTN_OK) return st;
+  if (!q || !k_cache || !v_cache || !kv_len || !out) return G4ATTN_ERR_NULL;
+  if (d->window != 0) return G4ATTN_ERR_UNSUPPORTED;          // sliding-window decode not built
+  if (d->num_q_heads / d->num_kv_heads > 16) return G4ATTN_ERR_UNSUPPORTED;
+  if (B < 1 || B > 65535 || max_kv_len < 1 || cache_cap < 1 || num_splits < 0) return G4ATTN_ERR_SHAPE;
+  if (max_kv_len > cache_cap) return G4ATTN_ERR_CACHE_OVERFLOW;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return G4ATTN_ERR_LAYOUT;
+  const int64_t c = decode_chunk(d, B, max_kv_len, num_splits);
+  const int64_t ns = ((int64_t)max_kv_len + c - 1) / c;
+  if (ns > 65535) return G4ATTN_ERR_SHAPE;
+  const size_t need = g4attn_decode_workspace_bytes(d, B, max_kv_len, num_splits);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return G4ATTN_ERR_WORKSPACE;
+
+  const size_t ph = (size_t)B * d->num_q_heads;
+  g4attn::DecodeArgs a{};
+  a.q = q; a.kc = k_cache; a.vc = v_cache; a.kv_len = kv_len; a.out = out; a.lse = lse;
+  a.o_part = (float*)workspace;
+  a.lse_part = (float*)((char*)workspace + align256(ph * ns * d->head_dim * sizeof(float)));
+  a.B = B; a.Hq = d->num_q_heads; a.Hkv = d->num_kv_heads; a.D = d->head_dim; a.cap = cache_cap;
+  a.nsplit = (int)ns; a.chunk = (int)c; a.max_len = max_kv_len;
+  a.scale_log2 = d->scale * g4attn::kLog2e;
+  return hip_status(g4attn::launch_decode(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

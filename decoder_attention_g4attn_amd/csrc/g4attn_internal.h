@@ -1,0 +1,132 @@
+// Internal helpers shared by the g4attn HIP kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace g4attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define G4_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return f2bf(lo) | (f2bf(hi) << 16);
+}
+__device__ __forceinline__ float bf2f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Wave-wide (64 lanes) reductions.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// XOR swizzle of 16-byte chunks inside each 256-byte LDS segment, keyed by
+// the tile row.  Rows 0..15 map to 16 distinct values (so 16 rows read at one
+// chunk hit 16 distinct bank groups), and rows {4a+e : e<4} map to 4e + a, so
+// the transposing reads (4 rows x 4 adjacent chunks per half-wave) are also
+// conflict-free.
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+__device__ __forceinline__ int phys_chunk(int chunk, int row) { return chunk ^ swz(row); }
+
+// One 16-byte-per-lane direct global->LDS copy: lane i's 16 bytes land at
+// lds_base + 16*i (lds_base must be wave-uniform).
+__device__ __forceinline__ void g2lds16(const void* gptr, G4_LDS void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gptr, lds_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 lds_read_b128(const G4_LDS char* p) {
+  return *(const G4_LDS bf16x8*)p;
+}
+// Transposing LDS read: see the lane mapping in the kernels that use it.
+__device__ __forceinline__ i16x4 lds_read_tr16(const G4_LDS char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((G4_LDS i16x4*)p);
+}
+__device__ __forceinline__ bf16x8 cat_tr(i16x4 a, i16x4 b) {
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 c = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, c);
+}
+
+__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+}  // namespace g4attn
+
+// Launchers (host side), defined in the kernel files.
+namespace g4attn {
+
+struct NormRopeArgs {
+  const uint16_t* x;
+  uint16_t* y;
+  const uint16_t* w;
+  int B, S, H, D, rot;
+  double log2_theta;
+  float eps;
+  int64_t xs[3], ys[3];
+  const int32_t* pos0;
+  int cache_cap;
+};
+hipError_t launch_norm_rope(const NormRopeArgs& a, hipStream_t st);
+
+struct KvPrepArgs {         // K=V prefill pre-pass
+  const uint16_t* x;        // [B, S, Hkv, 512] strided
+  const uint16_t* w_k;      // [512]
+  float* r;                 // [B, Hkv, S]
+  uint16_t* krot;           // [B, Hkv, S, 128]
+  int B, S, Hkv, rot;
+  double log2_theta;
+  float eps;
+  int64_t xs[3];
+};
+hipError_t launch_kv_prep(const KvPrepArgs& a, hipStream_t st);
+
+struct PrefillArgs {
+  const uint16_t* q;
+  const uint16_t* k;        // K, or X (K=V)
+  const uint16_t* v;        // V (NULL for K=V)
+  const uint16_t* w_k;      // K=V only
+  const float* r;           // K=V only: [B, Hkv, S]
+  const uint16_t* krot;     // K=V only: [B, Hkv, S, 128]
+  uint16_t* out;
+  float* lse;
+  int B, S, Hq, Hkv, D, window, kv_tied;
+  float scale_log2;         // scale * log2(e)
+  int64_t qs[3], ks[3], os[3];
+};
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
+
+struct DecodeArgs {
+  const uint16_t* q;        // [B, Hq, D]
+  const uint16_t* kc;       // [B, Hkv, cap, D]
+  const uint16_t* vc;
+  const int32_t* kv_len;    // [B]
+  uint16_t* out;            // [B, Hq, D]
+  float* lse;               // [B, Hq] or NULL
+  float* o_part;            // [B, Hq, nsplit, D]
+  float* lse_part;          // [B, Hq, nsplit]
+  int B, Hq, Hkv, D, cap, nsplit, chunk;
+  int max_len;              // host bound; kv_len values are clamped to [0, max_len]
+  float scale_log2;
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+
+}  // namespace g4attn

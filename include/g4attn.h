@@ -1,0 +1,200 @@
+/*
+ * g4attn - Gemma 4 decoder attention on AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels for one attention layer:
+ *   g4attn_norm_rope  - QK-norm / V-norm prologue (plain-weight RMSNorm) with
+ *                       full or zero-padded partial RoPE;
+ *   g4attn_prefill    - causal / sliding-window GQA softmax attention over a
+ *                       whole prompt, including the K=V global layer;
+ *   g4attn_decode     - one new query token per sequence over a KV cache
+ *                       (split-KV plus a log-sum-exp combine).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Tensors are bf16 (raw 16-bit patterns, uint16_t) unless stated; LSE
+ *   outputs are fp32 natural logs.
+ * - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *   library never allocates, frees, synchronises or prints.  Scratch memory
+ *   is a caller-provided workspace whose size the *_workspace_bytes query
+ *   returns.
+ * - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *   is stream-ordered.  No call blocks.
+ * - Every call validates all host-visible arguments BEFORE launching
+ *   anything and returns a g4attn_status.  On any error nothing is launched
+ *   and no memory is touched.  There is no fallback path.
+ * - Activation layout is [B, S, H, D] with the D stride equal to 1; the
+ *   batch, sequence and head strides are given in elements.  Base pointers
+ *   and strides must keep every row 16-byte aligned.
+ * - Thread-safe: the library keeps no state apart from a thread-local copy
+ *   of the last HIP error code.
+ *
+ * Source pages: "Gemma 4" (Keras port documentation), "gemma4-pt-claude"
+ * (PyTorch port README) and the vinija.ai "Gemma 4" primer.
+ */
+#ifndef G4ATTN_H
+#define G4ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t g4attn_bf16; /* raw bf16 bits */
+
+typedef enum {
+  G4ATTN_OK = 0,
+  G4ATTN_ERR_NULL = 1,           /* a required pointer is NULL                        */
+  G4ATTN_ERR_SHAPE = 2,          /* sizes inconsistent or out of range                */
+  G4ATTN_ERR_LAYOUT = 3,         /* misaligned pointer/stride, or non-unit D stride   */
+  G4ATTN_ERR_UNSUPPORTED = 4,    /* valid request this library does not implement     */
+  G4ATTN_ERR_CACHE_OVERFLOW = 5, /* a cache write or read would pass the capacity     */
+  G4ATTN_ERR_WORKSPACE = 6,      /* workspace NULL or smaller than required           */
+  G4ATTN_ERR_HIP = 7             /* a HIP launch failed; see g4attn_last_hip_error()  */
+} g4attn_status;
+
+/*
+ * One attention layer, after the argument table of the Keras port's
+ * Gemma4Model ("Gemma 4" docs, Gemma4Model table: num_heads, num_kv_heads /
+ * num_global_kv_heads, head_dim / global_head_dim, k_eq_v, sliding_window,
+ * partial_rotary_factor).
+ */
+typedef struct {
+  int32_t num_q_heads;  /* Hq; a multiple of num_kv_heads                                 */
+  int32_t num_kv_heads; /* Hkv; query head h uses KV head h / (Hq / Hkv)                  */
+  int32_t head_dim;     /* D: 256 (sliding layers) or 512 (global layers)                 */
+  int32_t window;       /* 0 = global (key j visible from row i iff j <= i);              */
+                        /* w > 0 = sliding (visible iff 0 <= i - j < w)                   */
+  int32_t k_eq_v;       /* prefill: 1 = K=V global layer (see g4attn_prefill)             */
+  int32_t rotary_dims;  /* rotated dims of q/k: head_dim (full), head_dim/4 (partial), 0  */
+  float rope_theta;     /* RoPE base: 1e4 on sliding layers, 1e6 on global layers         */
+  float rms_eps;        /* RMSNorm epsilon (1e-6)                                         */
+  float scale;          /* logits = scale * q.k (1/sqrt(head_dim) in the workloads)       */
+} g4attn_layer_desc;
+
+/*
+ * Prologue of one projection ("Gemma 4" docs, "What changed from Gemma 3":
+ * plain-weight RMSNorm and zero-pad partial rope; gemma4-pt-claude README,
+ * "Supported Models": QK-norm and V-norm on every variant; vinija.ai primer,
+ * "Dual RoPE configurations", rotation matrix):
+ *
+ *   r      = 1 / sqrt(mean_d x[b,t,h,d]^2 + rms_eps)
+ *   u_d    = x_d * r * weight_d            (weight NULL: u_d = x_d * r)
+ *   p      = (pos0 ? pos0[b] : 0) + t
+ *   f_j    = rope_theta^(-2j/D) for j < rotary_dims/2, else 0     (j < D/2)
+ *   y_j    = u_j cos(p f_j) - u_{j+D/2} sin(p f_j)
+ *   y_{j+D/2} = u_{j+D/2} cos(p f_j) + u_j sin(p f_j)
+ *
+ * computed in fp32 with the angle p*f_j formed and range-reduced in fp64,
+ * and rounded once to bf16 (round to nearest even).
+ *
+ *   x          [B, S, H, D] bf16, strides x_strides = {batch, seq, head}.
+ *   y          y_cache_cap == 0: [B, S, H, D] with strides y_strides;
+ *              y_cache_cap  > 0: a contiguous cache [B, H, y_cache_cap, D];
+ *              row p of sequence b, head h receives the result
+ *              (y_strides ignored).
+ *   weight     [D] bf16 or NULL (weightless; the V-norm).
+ *   head_dim   256 or 512; rotary_dims in {0, head_dim/4, head_dim}.
+ *   pos0       device int32 [B] (first position of each sequence) or NULL
+ *              (positions start at 0).
+ *   max_pos    host-known upper bound of every p (pos0[b] + S - 1); required
+ *              >= S - 1.  In cache mode max_pos >= y_cache_cap is
+ *              G4ATTN_ERR_CACHE_OVERFLOW (the cache raises rather than
+ *              evicting: gemma4-pt-claude README, "KV Cache").  The kernel
+ *              also skips any row outside [0, y_cache_cap).
+ * x and y may not overlap unless x == y with equal strides (in place).
+ */
+g4attn_status g4attn_norm_rope(const g4attn_bf16* x, g4attn_bf16* y, const g4attn_bf16* weight,
+                               int32_t B, int32_t S, int32_t H, int32_t head_dim,
+                               int32_t rotary_dims, float rope_theta, float rms_eps,
+                               const int64_t x_strides[3], const int64_t y_strides[3],
+                               const int32_t* pos0, int32_t max_pos, int32_t y_cache_cap,
+                               void* stream);
+
+/* Workspace (bytes) that g4attn_prefill needs for this layer and size. */
+size_t g4attn_prefill_workspace_bytes(const g4attn_layer_desc* desc, int32_t B, int32_t S);
+
+/*
+ * Prefill attention (vinija.ai primer, "Sliding-window attention" and
+ * "Global attention layers"; softmax of scaled dot products, "Why long
+ * context is difficult"):
+ *
+ *   s_ij   = scale * q_i . k_j,   j visible from i (see g4attn_layer_desc)
+ *   out_i  = sum_j softmax_j(s_ij) v_j,     lse_i = log sum_j exp(s_ij)
+ *
+ * for every batch b, query head h (KV head h / (Hq/Hkv)) and row i < S.
+ *
+ *   q          [B, S, Hq, D] post-prologue queries, strides q_strides.
+ *   k_eq_v == 0:
+ *     k, v     [B, S, Hkv, D] post-prologue keys and values, strides
+ *              kv_strides (shared by k and v); w_k ignored (may be NULL).
+ *   k_eq_v == 1 (global K=V layer; "Gemma 4" docs, "What changed from
+ *              Gemma 3", K=V global MQA):
+ *     k        [B, S, Hkv, D] the RAW tied projection X (before any norm),
+ *              strides kv_strides; v must be NULL; w_k [D] the K-norm weight.
+ *              Keys are RoPE(RMSNorm(X) * w_k) at positions 0..S-1 and
+ *              values are RMSNorm(X) (weightless), both formed inside the
+ *              call from one shared tile of X.  head_dim must be 512.
+ *   out        [B, S, Hq, D] bf16, strides o_strides.
+ *   lse        [B, Hq, S] fp32 (contiguous) or NULL.
+ *   workspace  >= g4attn_prefill_workspace_bytes(desc, B, S) bytes (16-byte
+ *              aligned); may be NULL when that is 0.
+ * Requires S >= 1, B >= 1.  Window and causality are applied exactly
+ * (integer logic); rows never see keys past themselves.
+ */
+g4attn_status g4attn_prefill(const g4attn_layer_desc* desc, const g4attn_bf16* q,
+                             const g4attn_bf16* k, const g4attn_bf16* v, const g4attn_bf16* w_k,
+                             g4attn_bf16* out, float* lse, int32_t B, int32_t S,
+                             const int64_t q_strides[3], const int64_t kv_strides[3],
+                             const int64_t o_strides[3], void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Workspace (bytes) that g4attn_decode needs; num_splits as passed to it. */
+size_t g4attn_decode_workspace_bytes(const g4attn_layer_desc* desc, int32_t B,
+                                     int32_t max_kv_len, int32_t num_splits);
+
+/*
+ * Single-token decode over a KV cache (vinija.ai primer, "KV cache and
+ * long-context scaling"; gemma4-pt-claude README, "KV Cache"):
+ *
+ *   out[b,h] = sum_{j < n_b} softmax_j(scale * q[b,h] . K[b,g,j]) V[b,g,j],
+ *   lse[b,h] = log sum_{j < n_b} exp(scale * q[b,h] . K[b,g,j]),
+ *   g = h / (Hq/Hkv),  n_b = kv_len[b]
+ *
+ *   q          [B, Hq, D] contiguous post-prologue queries (norm + RoPE at
+ *              the new token's position, e.g. via g4attn_norm_rope).
+ *   k_cache    [B, Hkv, cache_cap, D] contiguous post-prologue keys.
+ *   v_cache    same shape; may equal k_cache (one tensor serves as both).
+ *   kv_len     device int32 [B]; each value in [1, max_kv_len] (rows past a
+ *              sequence's n_b are never read).
+ *   max_kv_len host-known bound of kv_len; > cache_cap is
+ *              G4ATTN_ERR_CACHE_OVERFLOW.
+ *   out        [B, Hq, D] bf16 contiguous;  lse  [B, Hq] fp32 or NULL.
+ *   num_splits 0 = automatic; otherwise the KV range [0, max_kv_len) is cut
+ *              into num_splits equal chunks (a multiple of 64 rows each);
+ *              the partial results are merged by a log-sum-exp combine.
+ *   workspace  >= g4attn_decode_workspace_bytes(desc, B, max_kv_len,
+ *              num_splits) bytes, 16-byte aligned.
+ * Valid for window == 0 only (sliding-window decode is not built:
+ * G4ATTN_ERR_UNSUPPORTED).
+ */
+g4attn_status g4attn_decode(const g4attn_layer_desc* desc, const g4attn_bf16* q,
+                            const g4attn_bf16* k_cache, const g4attn_bf16* v_cache,
+                            const int32_t* kv_len, int32_t B, int32_t max_kv_len,
+                            int32_t cache_cap, g4attn_bf16* out, float* lse, int32_t num_splits,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* g4attn_status_str(g4attn_status status);
+
+/* The hipError_t of the last G4ATTN_ERR_HIP returned on this thread (0 if none). */
+int32_t g4attn_last_hip_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t g4attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* G4ATTN_H */

@@ -1,0 +1,137 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and rejects invalid calls on the host before any HIP call (no compute)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import decoder_attention_g4attn_amd as g4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "g4attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(g4.LIB_PATH), reason="libg4attn.so not built")
+
+FAKE = ctypes.c_void_p(0x100000)      # 16-byte aligned, never dereferenced
+MISALIGNED = ctypes.c_void_p(0x100008)
+I64 = ctypes.c_int64 * 3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\S.*?\b(g4attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    lib = g4.load()
+    decl = declared_functions()
+    assert set(decl) == set(g4.EXPORTED)
+    for name in decl:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    assert g4.g4attn_version() == 100
+    for s in range(8):
+        assert g4.g4attn_status_str(s)
+    assert g4.load().g4attn_last_hip_error() == 0
+
+
+def _desc(**kw):
+    d = dict(num_q_heads=32, num_kv_heads=4, head_dim=512, window=0, k_eq_v=False,
+             rotary_dims=128, rope_theta=1e6)
+    d.update(kw)
+    return g4.layer_desc(**d)
+
+
+def _prefill(desc, q=FAKE, k=FAKE, v=FAKE, wk=None, out=FAKE, B=1, S=16, qs=None, ks=None, os_=None,
+             ws=None, wsb=0):
+    lib = g4.load()
+    qs = qs or I64(16 * 32 * 512, 32 * 512, 512)
+    ks = ks or I64(16 * 4 * 512, 4 * 512, 512)
+    os_ = os_ or I64(16 * 32 * 512, 32 * 512, 512)
+    return lib.g4attn_prefill(ctypes.byref(desc), q, k, v, wk, out, None, B, S, qs, ks, os_, ws, wsb, None)
+
+
+def test_prefill_validation():
+    assert _prefill(_desc(), q=None) == g4.ERR_NULL
+    assert _prefill(_desc(), v=None) == g4.ERR_NULL
+    assert _prefill(_desc(num_q_heads=30)) == g4.ERR_SHAPE            # Hq % Hkv
+    assert _prefill(_desc(head_dim=128, rotary_dims=128)) == g4.ERR_UNSUPPORTED
+    assert _prefill(_desc(rotary_dims=100)) == g4.ERR_UNSUPPORTED
+    assert _prefill(_desc(window=-1)) == g4.ERR_SHAPE
+    assert _prefill(_desc(), S=0) == g4.ERR_SHAPE
+    assert _prefill(_desc(), B=0) == g4.ERR_SHAPE
+    assert _prefill(_desc(), q=MISALIGNED) == g4.ERR_LAYOUT
+    assert _prefill(_desc(), qs=I64(16 * 32 * 512, 32 * 512, 511)) == g4.ERR_LAYOUT
+    # K=V layer: one tensor, K weight required, D = 512 with 128 rotated dims
+    kv = _desc(k_eq_v=True)
+    assert _prefill(kv, wk=None, v=None) == g4.ERR_NULL
+    assert _prefill(kv, wk=FAKE, v=FAKE) == g4.ERR_SHAPE
+    assert _prefill(_desc(k_eq_v=True, rotary_dims=512), wk=FAKE, v=None) == g4.ERR_UNSUPPORTED
+    need = g4.g4attn_prefill_workspace_bytes(kv, 1, 16)
+    assert need == 256 + 16 * 4 * 128 * 2       # r (aligned to 256) + Krot
+    assert _prefill(kv, wk=FAKE, v=None) == g4.ERR_WORKSPACE
+    assert _prefill(kv, wk=FAKE, v=None, ws=FAKE, wsb=need - 1) == g4.ERR_WORKSPACE
+    assert g4.g4attn_prefill_workspace_bytes(_desc(), 1, 16) == 0
+
+
+def _decode(desc, B=2, max_len=100, cap=128, splits=0, ws=FAKE, wsb=1 << 30, q=FAKE, kc=FAKE, kl=FAKE):
+    lib = g4.load()
+    return lib.g4attn_decode(ctypes.byref(desc), q, kc, kc, kl, B, max_len, cap, FAKE, None, splits,
+                             ws, wsb, None)
+
+
+def test_decode_validation():
+    assert _decode(_desc(), q=None) == g4.ERR_NULL
+    assert _decode(_desc(), kl=None) == g4.ERR_NULL
+    assert _decode(_desc(), max_len=129, cap=128) == g4.ERR_CACHE_OVERFLOW    # cache overflow raises
+    assert _decode(_desc(window=1024)) == g4.ERR_UNSUPPORTED
+    assert _decode(_desc(num_q_heads=64, num_kv_heads=2)) == g4.ERR_UNSUPPORTED   # > 16 heads per group
+    assert _decode(_desc(), max_len=0) == g4.ERR_SHAPE
+    assert _decode(_desc(), splits=-1) == g4.ERR_SHAPE
+    assert _decode(_desc(), wsb=16) == g4.ERR_WORKSPACE
+    assert _decode(_desc(), ws=None) == g4.ERR_WORKSPACE
+    assert _decode(_desc(), kc=MISALIGNED) == g4.ERR_LAYOUT
+
+
+def test_decode_workspace_sizes():
+    d = _desc()
+    # automatic chunking: >= 256 rows, multiple of 64
+    ws = g4.g4attn_decode_workspace_bytes(d, 32, 131073, 0)
+    assert ws > 0
+    for splits in (1, 2, 7):
+        w = g4.g4attn_decode_workspace_bytes(d, 2, 1000, splits)
+        chunk = -(-(-(-1000 // splits)) // 64) * 64
+        ns = -(-1000 // chunk)
+        assert w == -(-2 * 32 * ns * 512 * 4 // 256) * 256 + -(-2 * 32 * ns * 4 // 256) * 256
+
+
+def test_norm_rope_validation():
+    lib = g4.load()
+    xs = I64(16 * 8 * 256, 8 * 256, 256)
+
+    def call(x=FAKE, y=FAKE, B=1, S=16, H=8, D=256, rot=256, theta=1e4, pos0=None, max_pos=15, cap=0,
+             strides=xs):
+        return lib.g4attn_norm_rope(x, y, None, B, S, H, D, rot, theta, 1e-6, strides, strides, pos0,
+                                    max_pos, cap, None)
+
+    assert call(x=None) == g4.ERR_NULL
+    assert call(S=0) == g4.ERR_SHAPE
+    assert call(D=128, rot=128) == g4.ERR_UNSUPPORTED
+    assert call(rot=96) == g4.ERR_UNSUPPORTED
+    assert call(theta=0.0) == g4.ERR_SHAPE
+    assert call(x=MISALIGNED) == g4.ERR_LAYOUT
+    assert call(strides=I64(16 * 8 * 256, 8 * 256, 255)) == g4.ERR_LAYOUT
+    # cache mode: the last written row must fit
+    assert call(cap=15) == g4.ERR_CACHE_OVERFLOW
+    assert call(pos0=FAKE, max_pos=40, cap=40) == g4.ERR_CACHE_OVERFLOW
+    assert call(pos0=FAKE, max_pos=10) == g4.ERR_SHAPE     # max_pos < S - 1
+
+
+def test_visible_pairs_host_logic_matches_oracle():
+    from oracle import attention as at
+    for S, w in [(1024, 512), (8192, 0), (16384, 1024), (32768, 0), (5, 8), (100, 1)]:
+        assert g4.visible_pairs(S, w) == at._pairs_closed(S, w)
