@@ -163,7 +163,7 @@ def g4attn_prefill(desc, q, k, v, out, w_k=None, lse=None, workspace=None, strea
     _check_bf16(q, k, v, out, w_k)
     B, S = q.shape[0], q.shape[1]
     need = lib.g4attn_prefill_workspace_bytes(ctypes.byref(desc), B, S)
-    if workspace is None and need:
+    if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.g4attn_prefill(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(w_k), _ptr(out),

@@ -121,10 +121,29 @@ g4attn_status g4attn_norm_rope(const g4attn_bf16* x, g4attn_bf16* y, const g4att
   return hip_status(g4attn::launch_norm_rope(a, (hipStream_t)stream));
 }
 
-size_t g4attn_prefill_workspace_bytes(const g4attn_layer_desc* d, int32_t B, int32_t S) {
-  if (!d || B < 1 || S < 1 || d->num_kv_heads < 1 || !d->k_eq_v) return 0;
+// Prefill workspace: per-row maxima + per-wave flags (all layers), then the
+// K=V inverse RMS and rotated slice.
+struct PrefillWs {
+  size_t mrow, flags, r, krot, total;
+};
+static PrefillWs prefill_ws(const g4attn_layer_desc* d, int32_t B, int32_t S) {
+  PrefillWs w{};
+  const int64_t G = d->num_q_heads / d->num_kv_heads;
+  const int64_t ntiles = ((int64_t)S * G + 127) / 128;
   const size_t rows = (size_t)B * d->num_kv_heads * S;
-  return align256(rows * sizeof(float)) + align256(rows * 128 * sizeof(uint16_t));
+  w.mrow = 0;
+  w.flags = align256((size_t)B * d->num_q_heads * S * sizeof(float));
+  w.r = w.flags + align256((size_t)B * d->num_kv_heads * ntiles * 4 * sizeof(int));
+  w.krot = w.r + (d->k_eq_v ? align256(rows * sizeof(float)) : 0);
+  w.total = w.krot + (d->k_eq_v ? align256(rows * 128 * sizeof(uint16_t)) : 0);
+  return w;
+}
+
+size_t g4attn_prefill_workspace_bytes(const g4attn_layer_desc* d, int32_t B, int32_t S) {
+  if (!d || B < 1 || S < 1 || d->num_kv_heads < 1 || d->num_q_heads < 1 ||
+      d->num_q_heads % d->num_kv_heads != 0)
+    return 0;
+  return prefill_ws(d, B, S).total;
 }
 
 g4attn_status g4attn_prefill(const g4attn_layer_desc* d, const g4attn_bf16* q,
@@ -149,9 +168,8 @@ g4attn_status g4attn_prefill(const g4attn_layer_desc* d, const g4attn_bf16* q,
       !aligned16(out) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
     return G4ATTN_ERR_LAYOUT;
   if (!strides_ok(q_strides) || !strides_ok(kv_strides) || !strides_ok(o_strides)) return G4ATTN_ERR_LAYOUT;
-  const size_t need = g4attn_prefill_workspace_bytes(d, B, S);
-  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
-    return G4ATTN_ERR_WORKSPACE;
+  const PrefillWs ws = prefill_ws(d, B, S);
+  if (!workspace || workspace_bytes < ws.total || !aligned16(workspace)) return G4ATTN_ERR_WORKSPACE;
 
   g4attn::PrefillArgs a{};
   a.q = q; a.k = k; a.v = v; a.w_k = w_k; a.out = out; a.lse = lse;
@@ -160,10 +178,12 @@ g4attn_status g4attn_prefill(const g4attn_layer_desc* d, const g4attn_bf16* q,
   a.scale_log2 = d->scale * g4attn::kLog2e;
   for (int i = 0; i < 3; ++i) { a.qs[i] = q_strides[i]; a.ks[i] = kv_strides[i]; a.os[i] = o_strides[i]; }
   hipStream_t s = (hipStream_t)stream;
+  char* wsp = (char*)workspace;
+  a.mrow = (float*)(wsp + ws.mrow);
+  a.flags = (int*)(wsp + ws.flags);
   if (d->k_eq_v) {
-    const size_t rows = (size_t)B * d->num_kv_heads * S;
-    float* r = (float*)workspace;
-    uint16_t* krot = (uint16_t*)((char*)workspace + align256(rows * sizeof(float)));
+    float* r = (float*)(wsp + ws.r);
+    uint16_t* krot = (uint16_t*)(wsp + ws.krot);
     g4attn::KvPrepArgs p{};
     p.x = k; p.w_k = w_k; p.r = r; p.krot = krot;
     p.B = B; p.S = S; p.Hkv = d->num_kv_heads; p.rot = d->rotary_dims;

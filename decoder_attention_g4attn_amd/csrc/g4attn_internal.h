@@ -40,14 +40,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// XOR swizzle of 16-byte chunks inside each 256-byte LDS segment, keyed by
-// the tile row.  Rows 0..15 map to 16 distinct values (so 16 rows read at one
-// chunk hit 16 distinct bank groups), and rows {4a+e : e<4} map to 4e + a, so
-// the transposing reads (4 rows x 4 adjacent chunks per half-wave) are also
-// conflict-free.
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
-__device__ __forceinline__ int phys_chunk(int chunk, int row) { return chunk ^ swz(row); }
-
 // One 16-byte-per-lane direct global->LDS copy: lane i's 16 bytes land at
 // lds_base + 16*i (lds_base must be wave-uniform).
 __device__ __forceinline__ void g2lds16(const void* gptr, G4_LDS void* lds_base) {
@@ -106,6 +98,8 @@ struct PrefillArgs {
   const uint16_t* w_k;      // K=V only
   const float* r;           // K=V only: [B, Hkv, S]
   const uint16_t* krot;     // K=V only: [B, Hkv, S, 128]
+  float* mrow;              // [B, Hq, S] true row maxima (log2 domain), written by the main pass
+  int* flags;               // [B, Hkv, ntiles, 4] per-wave reference-overflow flags
   uint16_t* out;
   float* lse;
   int B, S, Hq, Hkv, D, window, kv_tied;

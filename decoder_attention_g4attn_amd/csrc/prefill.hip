@@ -119,7 +119,9 @@ __device__ __forceinline__ void load_tile(const PrefillArgs& a, char* stage, int
   }
 }
 
-template <int D, bool TIED>
+// REDO = false: main pass.  REDO = true: recompute the workgroups whose main
+// pass flagged a reference overflow, with the row maxima the main pass found.
+template <int D, bool TIED, bool REDO>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   typedef Cfg<D, TIED> C;
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE];
@@ -144,6 +146,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 
   const int kt_lo = a.window ? max(0, tq0 - a.window + 1) / kBN : 0;
   const int kt_hi = tq1 / kBN;
+  int* wg_flags = a.flags + (((int64_t)b * a.Hkv + g) * ntiles + tile) * kWaves;
+  const int64_t mrow_idx = ((int64_t)b * a.Hq + head) * a.S + tq;
+  if (REDO) {
+    if ((wg_flags[0] | wg_flags[1] | wg_flags[2] | wg_flags[3]) == 0) return;
+  }
 
   // Prefetch the first tile, then load this lane's Q^T fragments.
   load_tile<D, TIED>(a, smem, kt_lo, b, g, wave, lane);
@@ -165,11 +172,6 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     }
   }
 
-  f32x16 oacc[C::NC];
-#pragma unroll
-  for (int c = 0; c < C::NC; ++c) oacc[c] = f32x16{};
-  float m_run = -INFINITY, l_part = 0.f;
-
   // Per-lane constant parts of the LDS addresses.
   const int k_rowoff = kv_row_off<D>(lr), k_x = kv_xor<D>(lr);
   const int kr_rowoff = kr_row_off(lr), kr_x = kr_xor(lr);
@@ -179,102 +181,119 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const int tr_chunk = 2 * (tG & 1) + (tqd >> 1);          // + 4 c
   const int tr_byte = (tqd & 1) * 8;
 
-  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-    __syncthreads();  // tile kt has landed in LDS; every wave is done with tile kt-1
-    char* cur = smem + ((kt - kt_lo) & 1) * C::STAGE;
-    if (kt < kt_hi) load_tile<D, TIED>(a, smem + ((kt - kt_lo + 1) & 1) * C::STAGE, kt + 1, b, g, wave, lane);
+  // Softmax with a fixed per-row reference: m_ref (log2 domain) is the row's
+  // maximum over its first tile with a visible key, and P = exp2(s - m_ref)
+  // is accumulated without ever rescaling O.  m_true tracks the real maximum;
+  // a wave whose rows end more than kHeadroom above m_ref flags its
+  // workgroup, which the REDO launch recomputes with m_ref = m_true (every
+  // P <= 1 then).
+  constexpr float kHeadroom = 64.f;
+  f32x16 oacc[C::NC];
+#pragma unroll
+  for (int c = 0; c < C::NC; ++c) oacc[c] = f32x16{};
+  float m_ref = -INFINITY, m_true = -INFINITY, l_part = 0.f;
+  if (REDO) m_ref = valid ? a.mrow[mrow_idx] : 0.f;
 
-    // ---- S^T = K Q^T (32 keys x 32 rows)
-    f32x16 sacc = f32x16{};
-#pragma unroll
-    for (int t = 0; t < C::NT; ++t) {
-      bf16x8 ka;
-      if (TIED && rot_step(t)) {
-        const int ch = (rot_chunk(t) + hh) ^ kr_x;
-        ka = lds_read_b128((const G4_LDS char*)(cur + C::KR_OFF + kr_rowoff + ch * 16));
-      } else {
-        const int ch = (2 * t + hh) ^ k_x;
-        ka = lds_read_b128((const G4_LDS char*)(cur + k_rowoff + ch * 16));
-      }
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[t], sacc, 0, 0, 0);
-    }
+  {
+    for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+      __syncthreads();  // tile kt has landed in LDS; every wave is done with tile kt-1
+      char* cur = smem + ((kt - kt_lo) & 1) * C::STAGE;
+      if (kt < kt_hi) load_tile<D, TIED>(a, smem + ((kt - kt_lo + 1) & 1) * C::STAGE, kt + 1, b, g, wave, lane);
 
-    // ---- scale (and K=V row factor), mask, online softmax
-    float rk[16];
-    if (TIED) {
+      // ---- S^T = K Q^T (32 keys x 32 rows)
+      f32x16 sacc = f32x16{};
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const f32x4 v = *(const G4_LDS f32x4*)(cur + C::R_OFF + (8 * gq + 4 * hh) * 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) rk[4 * gq + i] = v[i];
+      for (int t = 0; t < C::NT; ++t) {
+        bf16x8 ka;
+        if (TIED && rot_step(t)) {
+          const int ch = (rot_chunk(t) + hh) ^ kr_x;
+          ka = lds_read_b128((const G4_LDS char*)(cur + C::KR_OFF + kr_rowoff + ch * 16));
+        } else {
+          const int ch = (2 * t + hh) ^ k_x;
+          ka = lds_read_b128((const G4_LDS char*)(cur + k_rowoff + ch * 16));
+        }
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[t], sacc, 0, 0, 0);
+        if ((t & 3) == 3) __builtin_amdgcn_sched_barrier(0);
       }
-    }
-    float s[16];
+
+      // ---- scale (and K=V row factor), mask, exponentiate against m_ref
+      float rk[16];
+      if (TIED) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = sacc[r] * a.scale_log2 * (TIED ? rk[r] : 1.f);
-    const int key0 = kt * kBN;
-    const bool full = (key0 + kBN - 1 <= tq0) && (a.window == 0 || key0 >= tq1 - a.window + 1);
-    if (!full) {
+        for (int gq = 0; gq < 4; ++gq) {
+          const f32x4 v = *(const G4_LDS f32x4*)(cur + C::R_OFF + (8 * gq + 4 * hh) * 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) rk[4 * gq + i] = v[i];
+        }
+      }
+      float s[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = sacc[r] * a.scale_log2 * (TIED ? rk[r] : 1.f);
+      const int key0 = kt * kBN;
+      const bool full = (key0 + kBN - 1 <= tq0) && (a.window == 0 || key0 >= tq1 - a.window + 1);
+      if (!full) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const int d = tq - key;
+          const bool vis = d >= 0 && (a.window == 0 || d < a.window);
+          s[r] = vis ? s[r] : -INFINITY;
+        }
+      }
+      float mx = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      m_true = fmaxf(m_true, mx);
+      if (!REDO && __builtin_amdgcn_ballot_w64(m_ref == -INFINITY)) {  // a row meets its first visible key
+        const float rowmx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        m_ref = m_ref == -INFINITY ? rowmx : m_ref;
+      }
+      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+      float p[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = key0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-        const int d = tq - key;
-        const bool vis = d >= 0 && (a.window == 0 || d < a.window);
-        s[r] = vis ? s[r] : -INFINITY;
+        p[r] = __builtin_amdgcn_exp2f(s[r] - m_use);
+        l_part += p[r];
       }
-    }
-    float mx = s[0];
+      bf16x8 pb[2];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
-    float psum = 0.f;
-    float p[16];
+      for (int mm = 0; mm < 2; ++mm) {
+        u32x4 w;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      p[r] = __builtin_amdgcn_exp2f(s[r] - m_use);
-      psum += p[r];
-    }
-    l_part = l_part * alpha + psum;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-      for (int c = 0; c < C::NC; ++c)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[c][r] *= alpha;
-    }
-    bf16x8 pb[2];
-#pragma unroll
-    for (int mm = 0; mm < 2; ++mm) {
-      u32x4 w;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r0 = 8 * mm + 2 * i;
-        const float p0 = TIED ? p[r0] * rk[r0] : p[r0];
-        const float p1 = TIED ? p[r0 + 1] * rk[r0 + 1] : p[r0 + 1];
-        w[i] = pack_bf2(p0, p1);
+        for (int i = 0; i < 4; ++i) {
+          const int r0 = 8 * mm + 2 * i;
+          const float p0 = TIED ? p[r0] * rk[r0] : p[r0];
+          const float p1 = TIED ? p[r0 + 1] * rk[r0 + 1] : p[r0 + 1];
+          w[i] = pack_bf2(p0, p1);
+        }
+        pb[mm] = __builtin_bit_cast(bf16x8, w);
       }
-      pb[mm] = __builtin_bit_cast(bf16x8, w);
-    }
 
-    // ---- O^T += V^T P^T
-    const char* vt = TIED ? cur : cur + C::KT_BYTES;
+      // ---- O^T += V^T P^T
+      const char* vt = TIED ? cur : cur + C::KT_BYTES;
 #pragma unroll
-    for (int mm = 0; mm < 2; ++mm) {
-      const int R0 = 16 * mm + tr_row0, R1 = R0 + 8;
-      const char* p0 = vt + kv_row_off<D>(R0) + tr_byte;
-      const char* p1 = vt + kv_row_off<D>(R1) + tr_byte;
-      const int x0 = kv_xor<D>(R0), x1 = kv_xor<D>(R1);
+      for (int mm = 0; mm < 2; ++mm) {
+        const int R0 = 16 * mm + tr_row0, R1 = R0 + 8;
+        const char* p0 = vt + kv_row_off<D>(R0) + tr_byte;
+        const char* p1 = vt + kv_row_off<D>(R1) + tr_byte;
+        const int x0 = kv_xor<D>(R0), x1 = kv_xor<D>(R1);
 #pragma unroll
-      for (int c = 0; c < C::NC; ++c) {
-        const int ch = 4 * c + tr_chunk;
-        const i16x4 lo = lds_read_tr16((const G4_LDS char*)(p0 + (ch ^ x0) * 16));
-        const i16x4 hi = lds_read_tr16((const G4_LDS char*)(p1 + (ch ^ x1) * 16));
-        oacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cat_tr(lo, hi), pb[mm], oacc[c], 0, 0, 0);
+        for (int c = 0; c < C::NC; ++c) {
+          const int ch = 4 * c + tr_chunk;
+          const i16x4 lo = lds_read_tr16((const G4_LDS char*)(p0 + (ch ^ x0) * 16));
+          const i16x4 hi = lds_read_tr16((const G4_LDS char*)(p1 + (ch ^ x1) * 16));
+          oacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cat_tr(lo, hi), pb[mm], oacc[c], 0, 0, 0);
+          if ((c & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
+  }
+
+  if (!REDO) {
+    const float mt = fmaxf(m_true, __shfl_xor(m_true, 32, 64));
+    const bool over = mt > m_ref + kHeadroom;
+    if (lane == 0) wg_flags[wave] = __builtin_amdgcn_ballot_w64(over) != 0;
+    if (valid && hh == 0) a.mrow[mrow_idx] = mt;
   }
 
   // ---- epilogue: normalise, round once to bf16, store
@@ -294,7 +313,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   }
   if (a.lse && hh == 0) {
     a.lse[((int64_t)b * a.Hq + head) * a.S + tq] =
-        l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+        l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
@@ -304,13 +323,20 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
   const int64_t ntiles = ((int64_t)a.S * G + kBM - 1) / kBM;
   const dim3 grid((unsigned)ntiles, (unsigned)a.Hkv, (unsigned)a.B);
-  if (a.kv_tied)
-    hipLaunchKernelGGL((prefill_kernel<512, true>), grid, dim3(256), 0, st, a);
-  else if (a.D == 512)
-    hipLaunchKernelGGL((prefill_kernel<512, false>), grid, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((prefill_kernel<256, false>), grid, dim3(256), 0, st, a);
-  return hipGetLastError();
+  for (int redo = 0; redo < 2; ++redo) {
+    if (a.kv_tied)
+      hipLaunchKernelGGL((redo ? prefill_kernel<512, true, true> : prefill_kernel<512, true, false>), grid,
+                         dim3(256), 0, st, a);
+    else if (a.D == 512)
+      hipLaunchKernelGGL((redo ? prefill_kernel<512, false, true> : prefill_kernel<512, false, false>), grid,
+                         dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((redo ? prefill_kernel<256, false, true> : prefill_kernel<256, false, false>), grid,
+                         dim3(256), 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace g4attn

@@ -138,8 +138,9 @@ size_t g4attn_prefill_workspace_bytes(const g4attn_layer_desc* desc, int32_t B, 
  *              call from one shared tile of X.  head_dim must be 512.
  *   out        [B, S, Hq, D] bf16, strides o_strides.
  *   lse        [B, Hq, S] fp32 (contiguous) or NULL.
- *   workspace  >= g4attn_prefill_workspace_bytes(desc, B, S) bytes (16-byte
- *              aligned); may be NULL when that is 0.
+ *   workspace  >= g4attn_prefill_workspace_bytes(desc, B, S) bytes, 16-byte
+ *              aligned (per-row softmax maxima and flags; for K=V also the
+ *              inverse RMS and rotated slice of each key row).
  * Requires S >= 1, B >= 1.  Window and causality are applied exactly
  * (integer logic); rows never see keys past themselves.
  */

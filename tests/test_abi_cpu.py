@@ -72,10 +72,12 @@ def test_prefill_validation():
     assert _prefill(kv, wk=FAKE, v=FAKE) == g4.ERR_SHAPE
     assert _prefill(_desc(k_eq_v=True, rotary_dims=512), wk=FAKE, v=None) == g4.ERR_UNSUPPORTED
     need = g4.g4attn_prefill_workspace_bytes(kv, 1, 16)
-    assert need == 256 + 16 * 4 * 128 * 2       # r (aligned to 256) + Krot
+    # row maxima [1, 32, 16] fp32 + flags [1, 4, 1 tile, 4 waves] + r [1, 4, 16] + Krot [1, 4, 16, 128]
+    assert need == 2048 + 256 + 256 + 16 * 4 * 128 * 2
     assert _prefill(kv, wk=FAKE, v=None) == g4.ERR_WORKSPACE
     assert _prefill(kv, wk=FAKE, v=None, ws=FAKE, wsb=need - 1) == g4.ERR_WORKSPACE
-    assert g4.g4attn_prefill_workspace_bytes(_desc(), 1, 16) == 0
+    assert g4.g4attn_prefill_workspace_bytes(_desc(), 1, 16) == 2048 + 256
+    assert _prefill(_desc()) == g4.ERR_WORKSPACE
 
 
 def _decode(desc, B=2, max_len=100, cap=128, splits=0, ws=FAKE, wsb=1 << 30, q=FAKE, kc=FAKE, kl=FAKE):

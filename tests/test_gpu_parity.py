@@ -266,3 +266,39 @@ def test_decode_equals_prefill_row(gpu_lib):
         kl = torch.tensor([t + 1], dtype=torch.int32, device=DEV)
         g4.g4attn_decode(g4.layer_desc(Hq, Hkv, D), q[:, t].contiguous(), kc, vc, kl, t + 1, out)
         assert (out.float() - pre[:, t].float()).abs().max().item() < 2e-2
+
+
+@pytest.mark.parametrize("D,w,kv_tied", [(256, 0, False), (512, 0, False), (256, 200, False), (512, 0, True)])
+def test_prefill_reference_overflow_redo(gpu_lib, D, w, kv_tied):
+    """Logits that grow along the sequence far past the first tile's maximum
+    (q = e_0, k_j = j/2 e_0, scale 1) force the recomputation pass."""
+    g4 = gpu_lib
+    B, S, Hq, Hkv = 1, 300, 8, 1
+    q = torch.zeros((B, S, Hq, D), dtype=torch.bfloat16, device=DEV)
+    q[..., 0] = 1.0
+    j = torch.arange(S, device=DEV, dtype=torch.float32)
+    k = torch.zeros((B, S, Hkv, D), dtype=torch.bfloat16, device=DEV)
+    k[0, :, 0, 0] = (0.5 * j).to(torch.bfloat16)
+    v = _bf((B, S, Hkv, D), 81)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=DEV)
+    if not kv_tied:
+        desc = g4.layer_desc(Hq, Hkv, D, window=w, scale=1.0)
+        g4.g4attn_prefill(desc, q, k, v, out, lse=lse)
+        ro, rl = oat.attention_band(f64(q), f64(k), f64(v), 1.0, w)
+    else:
+        # K=V: X ~ N(0,1) except coordinate 101 (not rotated) = j/128, unit
+        # weights.  The norm keeps K_101 close to j/128, so the logits 80 K_101
+        # rise by ~170 after the first tile, while values stay O(1).
+        X = _bf((B, S, Hkv, D), 82)
+        X[0, :, 0, 101] = (j / 128).to(torch.bfloat16)
+        q2 = torch.zeros_like(q)
+        q2[..., 101] = 80.0
+        wk = torch.ones(D, dtype=torch.bfloat16, device=DEV)
+        desc = g4.layer_desc(Hq, Hkv, D, k_eq_v=True, rotary_dims=128, rope_theta=1e6, scale=1.0)
+        g4.g4attn_prefill(desc, q2, X, None, out, w_k=wk, lse=lse)
+        K, V = onr.kv_tied_k_v(f64(X), f64(wk), np.tile(np.arange(S), (B, 1)), 128, 1e6)
+        ro, rl = oat.attention_band(f64(q2), K, V, 1.0, 0)
+    torch.cuda.synchronize()
+    assert_parity(f64(out), ro, f"redo D={D} w={w} tied={kv_tied}")
+    np.testing.assert_allclose(lse.cpu().numpy(), rl, rtol=1e-4, atol=2e-3)
