@@ -65,18 +65,20 @@ __device__ __forceinline__ int kr_xor(int R) { return (R >> 2) & 3; }
 
 // Is the 16-dim k-step t one of the rotated (Krot) dims 0..63 / 256..319?
 __device__ __forceinline__ constexpr bool rot_step(int t) { return t < 4 || (t >= 16 && t < 20); }
-__device__ __forceinline__ constexpr int rot_chunk(int t) { return t < 4 ? 2 * t : 8 + 2 * (t - 16); }
 
+// Global->LDS copy of key tile kt.  Each row's base address is wave-uniform
+// (scalar registers) and lanes add an unsigned 32-bit byte offset, which maps
+// onto the scalar-base form of the load.
 template <int D, bool TIED>
 __device__ __forceinline__ void load_tile(const PrefillArgs& a, char* stage, int kt, int b, int g,
                                           int wave, int lane) {
   typedef Cfg<D, TIED> C;
   const int key0 = kt * kBN;
   const int64_t kb = b * a.ks[0] + g * a.ks[2];
-  auto key_ptr = [&](const uint16_t* base, int R) {
+  auto row_base = [&](const uint16_t* base, int R) {
     int key = key0 + R;
     key = key < a.S ? key : a.S - 1;  // rows past S are masked; stay in bounds
-    return base + kb + key * a.ks[1];
+    return (const char*)(base + kb + key * a.ks[1]);
   };
   const int ntile = TIED ? 1 : 2;
 #pragma unroll
@@ -87,37 +89,46 @@ __device__ __forceinline__ void load_tile(const PrefillArgs& a, char* stage, int
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int R = wave * 8 + i;
-        const int ch = lane ^ kv_xor<D>(R);
-        g2lds16(key_ptr(src, R) + ch * 8, (G4_LDS void*)(tile + kv_row_off<D>(R)));
+        const uint32_t off = (uint32_t)(lane ^ kv_xor<D>(R)) * 16u;
+        g2lds16(row_base(src, R) + off, (G4_LDS void*)(tile + kv_row_off<D>(R)));
       }
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        // lanes 0..31 copy row s, lanes 32..63 row s + 16 (rows are clamped
+        // independently, so the second row's offset is measured from the first)
         const int s = wave * 4 + i;
-        const int R = s + 16 * (lane >> 5);
-        const int ch = (lane & 31) ^ kv_xor<D>(R);
-        g2lds16(key_ptr(src, R) + ch * 8, (G4_LDS void*)(tile + s * kSeg));
+        const char* b0 = row_base(src, s);
+        const uint32_t d = (uint32_t)(row_base(src, s + 16) - b0);
+        const uint32_t off = (lane >> 5) * d + (uint32_t)((lane & 31) ^ kv_xor<D>(s)) * 16u;
+        g2lds16(b0 + off, (G4_LDS void*)(tile + s * kSeg));
       }
     }
   }
   if (TIED) {
     const int64_t rowbase = ((int64_t)b * a.Hkv + g) * a.S;
+    const int kfirst = min(key0, a.S - 1);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int s = wave * 2 + i;
+      // lanes 16q .. 16q+15 copy Krot row s + 8q
       const int R = s + 8 * (lane >> 4);
-      int key = key0 + R;
-      key = key < a.S ? key : a.S - 1;
-      const int ch = (lane & 15) ^ kr_xor(R);
-      g2lds16(a.krot + (rowbase + key) * 128 + ch * 8, (G4_LDS void*)(stage + C::KR_OFF + s * kSeg));
+      const int key = min(key0 + R, a.S - 1);
+      const uint32_t off = (uint32_t)(key - kfirst) * 256u + (uint32_t)((lane & 15) ^ kr_xor(R)) * 16u;
+      g2lds16((const char*)(a.krot + (rowbase + kfirst) * 128) + off, (G4_LDS void*)(stage + C::KR_OFF + s * kSeg));
     }
     if (wave == 0) {
-      int key = key0 + (lane & 31);
-      key = key < a.S ? key : a.S - 1;
-      __builtin_amdgcn_global_load_lds(a.r + rowbase + key, (G4_LDS void*)(stage + C::R_OFF), 4, 0, 0);
+      const int key = min(key0 + (lane & 31), a.S - 1);
+      __builtin_amdgcn_global_load_lds((const char*)(a.r + rowbase + kfirst) + (uint32_t)(key - kfirst) * 4u,
+                                       (G4_LDS void*)(stage + C::R_OFF), 4, 0, 0);
     }
   }
 }
+
+// Scheduling-group masks (LLVM AMDGPU): MFMA, LDS read.
+constexpr int kSgMfma = 0x008;
+constexpr int kSgDsRead = 0x100;
+constexpr int kLook = 3;  // LDS operand reads issued ahead of their MFMA
 
 // REDO = false: main pass.  REDO = true: recompute the workgroups whose main
 // pass flagged a reference overflow, with the row maxima the main pass found.
@@ -126,7 +137,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   typedef Cfg<D, TIED> C;
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE];
 
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int hh = lane >> 5;   // lane half
   const int lr = lane & 31;   // row within the wave
@@ -147,21 +158,21 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const int kt_lo = a.window ? max(0, tq0 - a.window + 1) / kBN : 0;
   const int kt_hi = tq1 / kBN;
   int* wg_flags = a.flags + (((int64_t)b * a.Hkv + g) * ntiles + tile) * kWaves;
-  const int64_t mrow_idx = ((int64_t)b * a.Hq + head) * a.S + tq;
   if (REDO) {
     if ((wg_flags[0] | wg_flags[1] | wg_flags[2] | wg_flags[3]) == 0) return;
   }
 
-  // Prefetch the first tile, then load this lane's Q^T fragments.
+  // Prefetch the first tile, then load this lane's Q^T fragments (rows past S
+  // read row S-1; their results are never stored).
   load_tile<D, TIED>(a, smem, kt_lo, b, g, wave, lane);
 
   bf16x8 qf[C::NT];
   {
-    const uint16_t* qrow = a.q + b * a.qs[0] + (int64_t)(valid ? tq : 0) * a.qs[1] + head * a.qs[2];
+    const uint16_t* qrow = a.q + b * a.qs[0] + (int64_t)min(tq, a.S - 1) * a.qs[1] + head * a.qs[2];
 #pragma unroll
     for (int t = 0; t < C::NT; ++t) {
       const int d0 = 16 * t + 8 * hh;
-      u32x4 raw = valid ? *(const u32x4*)(qrow + d0) : u32x4{0, 0, 0, 0};
+      u32x4 raw = *(const u32x4*)(qrow + d0);
       if (TIED && !rot_step(t)) {
         const u32x4 w = *(const u32x4*)(a.w_k + d0);
 #pragma unroll
@@ -172,14 +183,28 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     }
   }
 
-  // Per-lane constant parts of the LDS addresses.
-  const int k_rowoff = kv_row_off<D>(lr), k_x = kv_xor<D>(lr);
-  const int kr_rowoff = kr_row_off(lr), kr_x = kr_xor(lr);
-  // transposing read: issuing lane -> (row, chunk) of the 4x16 block it feeds
+  // Per-lane LDS byte offsets within a stage.  QK^T operand (K row lr, dims
+  // 16t + 8hh ..): chunk (2t + hh) ^ x keeps t>>1 in the high bits, so the
+  // address is koff[t & 1] + 64 (t >> 1).
+  const int k_x = kv_xor<D>(lr), kr_x = kr_xor(lr);
+  const int koff0 = kv_row_off<D>(lr) + 16 * (hh ^ k_x);
+  const int koff1 = kv_row_off<D>(lr) + 16 * ((2 + hh) ^ k_x);
+  const int kroff0 = C::KR_OFF + kr_row_off(lr) + 16 * (hh ^ kr_x);
+  const int kroff1 = C::KR_OFF + kr_row_off(lr) + 16 * ((2 + hh) ^ kr_x);
+  // PV operand (transposing read): issuing lane feeds row 16m + 8u + r0 of
+  // dim block c at 64c + toff[m][u].
   const int tG = lane >> 4, te = (lane >> 2) & 3, tqd = lane & 3;
-  const int tr_row0 = 4 * (tG >> 1) + te;                  // + 16 m + 8 u
-  const int tr_chunk = 2 * (tG & 1) + (tqd >> 1);          // + 4 c
-  const int tr_byte = (tqd & 1) * 8;
+  const int tr_row0 = 4 * (tG >> 1) + te;
+  const int tr_chunk = 2 * (tG & 1) + (tqd >> 1);
+  const int vbase = TIED ? 0 : C::KT_BYTES;
+  int toff[2][2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int R = 16 * m + 8 * u + tr_row0;
+      toff[m][u] = vbase + kv_row_off<D>(R) + (tqd & 1) * 8 + 16 * (tr_chunk ^ kv_xor<D>(R));
+    }
 
   // Softmax with a fixed per-row reference: m_ref (log2 domain) is the row's
   // maximum over its first tile with a visible key, and P = exp2(s - m_ref)
@@ -192,100 +217,107 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
   for (int c = 0; c < C::NC; ++c) oacc[c] = f32x16{};
   float m_ref = -INFINITY, m_true = -INFINITY, l_part = 0.f;
+  const int64_t mrow_idx = ((int64_t)b * a.Hq + head) * a.S + tq;
   if (REDO) m_ref = valid ? a.mrow[mrow_idx] : 0.f;
 
-  {
-    for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-      __syncthreads();  // tile kt has landed in LDS; every wave is done with tile kt-1
-      char* cur = smem + ((kt - kt_lo) & 1) * C::STAGE;
-      if (kt < kt_hi) load_tile<D, TIED>(a, smem + ((kt - kt_lo + 1) & 1) * C::STAGE, kt + 1, b, g, wave, lane);
+  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+    __syncthreads();  // tile kt has landed in LDS; every wave is done with tile kt-1
+    const int so = ((kt - kt_lo) & 1) * C::STAGE;
+    const G4_LDS char* cur = (const G4_LDS char*)smem + so;
+    if (kt < kt_hi) load_tile<D, TIED>(a, smem + (C::STAGE - so), kt + 1, b, g, wave, lane);
 
-      // ---- S^T = K Q^T (32 keys x 32 rows)
-      f32x16 sacc = f32x16{};
-#pragma unroll
-      for (int t = 0; t < C::NT; ++t) {
-        bf16x8 ka;
-        if (TIED && rot_step(t)) {
-          const int ch = (rot_chunk(t) + hh) ^ kr_x;
-          ka = lds_read_b128((const G4_LDS char*)(cur + C::KR_OFF + kr_rowoff + ch * 16));
-        } else {
-          const int ch = (2 * t + hh) ^ k_x;
-          ka = lds_read_b128((const G4_LDS char*)(cur + k_rowoff + ch * 16));
-        }
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[t], sacc, 0, 0, 0);
-        if ((t & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+    // ---- S^T = K Q^T (32 keys x 32 rows), two accumulators, reads kLook ahead
+    auto kread = [&](int t) -> bf16x8 {
+      if (TIED && rot_step(t)) {  // Krot chunk 2u + hh, u = t (t < 4) or t - 12
+        const int u = t < 4 ? t : t - 12;
+        return lds_read_b128(cur + ((u & 1) ? kroff1 : kroff0) + 64 * (u >> 1));
       }
+      return lds_read_b128(cur + ((t & 1) ? koff1 : koff0) + 64 * (t >> 1));
+    };
+    bf16x8 ka[kLook + 1];
+#pragma unroll
+    for (int t = 0; t < kLook; ++t) ka[t] = kread(t);
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, kLook, 0);
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t) {
+      if (t + kLook < C::NT) ka[(t + kLook) % (kLook + 1)] = kread(t + kLook);
+      if (t & 1)
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % (kLook + 1)], qf[t], s1, 0, 0, 0);
+      else
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % (kLook + 1)], qf[t], s0, 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      if (t + kLook < C::NT) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+    }
 
-      // ---- scale (and K=V row factor), mask, exponentiate against m_ref
-      float rk[16];
-      if (TIED) {
+    // ---- scale (and K=V row factor), mask, exponentiate against m_ref
+    float rk[16];
+    if (TIED) {
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const f32x4 v = *(const G4_LDS f32x4*)(cur + C::R_OFF + (8 * gq + 4 * hh) * 4);
+      for (int gq = 0; gq < 4; ++gq) {
+        const f32x4 v = *(const G4_LDS f32x4*)(cur + C::R_OFF + (8 * gq + 4 * hh) * 4);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) rk[4 * gq + i] = v[i];
-        }
+        for (int i = 0; i < 4; ++i) rk[4 * gq + i] = v[i];
       }
-      float s[16];
+    }
+    float sv[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = sacc[r] * a.scale_log2 * (TIED ? rk[r] : 1.f);
-      const int key0 = kt * kBN;
-      const bool full = (key0 + kBN - 1 <= tq0) && (a.window == 0 || key0 >= tq1 - a.window + 1);
-      if (!full) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const int d = tq - key;
-          const bool vis = d >= 0 && (a.window == 0 || d < a.window);
-          s[r] = vis ? s[r] : -INFINITY;
-        }
-      }
-      float mx = s[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-      m_true = fmaxf(m_true, mx);
-      if (!REDO && __builtin_amdgcn_ballot_w64(m_ref == -INFINITY)) {  // a row meets its first visible key
-        const float rowmx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        m_ref = m_ref == -INFINITY ? rowmx : m_ref;
-      }
-      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-      float p[16];
+    for (int r = 0; r < 16; ++r) sv[r] = (s0[r] + s1[r]) * a.scale_log2 * (TIED ? rk[r] : 1.f);
+    const int key0 = kt * kBN;
+    const bool full = (key0 + kBN - 1 <= tq0) && (a.window == 0 || key0 >= tq1 - a.window + 1);
+    if (!full) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        p[r] = __builtin_amdgcn_exp2f(s[r] - m_use);
-        l_part += p[r];
+        const int key = key0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        const int d = tq - key;
+        const bool vis = d >= 0 && (a.window == 0 || d < a.window);
+        sv[r] = vis ? sv[r] : -INFINITY;
       }
-      bf16x8 pb[2];
+    }
+    float mx = sv[0];
 #pragma unroll
-      for (int mm = 0; mm < 2; ++mm) {
-        u32x4 w;
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sv[r]);
+    m_true = fmaxf(m_true, mx);
+    if (!REDO && __builtin_amdgcn_ballot_w64(m_ref == -INFINITY)) {  // a row meets its first visible key
+      const float rowmx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      m_ref = m_ref == -INFINITY ? rowmx : m_ref;
+    }
+    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+    bf16x8 pb[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r0 = 8 * mm + 2 * i;
-          const float p0 = TIED ? p[r0] * rk[r0] : p[r0];
-          const float p1 = TIED ? p[r0 + 1] * rk[r0 + 1] : p[r0 + 1];
-          w[i] = pack_bf2(p0, p1);
-        }
-        pb[mm] = __builtin_bit_cast(bf16x8, w);
+    for (int mm = 0; mm < 2; ++mm) {
+      u32x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r0 = 8 * mm + 2 * i;
+        float p0 = __builtin_amdgcn_exp2f(sv[r0] - m_use);
+        float p1 = __builtin_amdgcn_exp2f(sv[r0 + 1] - m_use);
+        l_part += p0 + p1;
+        if (TIED) { p0 *= rk[r0]; p1 *= rk[r0 + 1]; }
+        w[i] = pack_bf2(p0, p1);
       }
+      pb[mm] = __builtin_bit_cast(bf16x8, w);
+    }
 
-      // ---- O^T += V^T P^T
-      const char* vt = TIED ? cur : cur + C::KT_BYTES;
+    // ---- O^T += V^T P^T, transposing reads kLook MFMAs ahead
+    constexpr int NPV = 2 * C::NC;  // (mm, c) pairs
+    auto vread = [&](int i) -> bf16x8 {
+      const int mm = i / C::NC, c = i % C::NC;
+      const i16x4 lo = lds_read_tr16(cur + toff[mm][0] + 64 * c);
+      const i16x4 hi = lds_read_tr16(cur + toff[mm][1] + 64 * c);
+      return cat_tr(lo, hi);
+    };
+    bf16x8 va[kLook + 1];
 #pragma unroll
-      for (int mm = 0; mm < 2; ++mm) {
-        const int R0 = 16 * mm + tr_row0, R1 = R0 + 8;
-        const char* p0 = vt + kv_row_off<D>(R0) + tr_byte;
-        const char* p1 = vt + kv_row_off<D>(R1) + tr_byte;
-        const int x0 = kv_xor<D>(R0), x1 = kv_xor<D>(R1);
+    for (int i = 0; i < kLook; ++i) va[i] = vread(i);
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2 * kLook, 0);
 #pragma unroll
-        for (int c = 0; c < C::NC; ++c) {
-          const int ch = 4 * c + tr_chunk;
-          const i16x4 lo = lds_read_tr16((const G4_LDS char*)(p0 + (ch ^ x0) * 16));
-          const i16x4 hi = lds_read_tr16((const G4_LDS char*)(p1 + (ch ^ x1) * 16));
-          oacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cat_tr(lo, hi), pb[mm], oacc[c], 0, 0, 0);
-          if ((c & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-        }
-      }
+    for (int i = 0; i < NPV; ++i) {
+      if (i + kLook < NPV) va[(i + kLook) % (kLook + 1)] = vread(i + kLook);
+      const int mm = i / C::NC, c = i % C::NC;
+      oacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % (kLook + 1)], pb[mm], oacc[c], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      if (i + kLook < NPV) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
     }
   }
 
