@@ -62,11 +62,15 @@ _I64x3 = ctypes.c_int64 * 3
 
 
 def load(path=None):
-    """Load libg4attn.so (once).  Raises if it has not been built."""
+    """Load libg4attn.so (once).  Raises if it has not been built.
+
+    ``path`` or the environment variable ``G4ATTN_LIB`` selects another build
+    of the same library.
+    """
     global _lib
     if _lib is not None:
         return _lib
-    path = path or LIB_PATH
+    path = path or os.environ.get("G4ATTN_LIB") or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(f"libg4attn.so not built ({path}); run "
                            "`python -m decoder_attention_g4attn_amd.build`")

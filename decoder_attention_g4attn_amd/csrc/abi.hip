@@ -205,7 +205,9 @@ size_t g4attn_decode_workspace_bytes(const g4attn_layer_desc* d, int32_t B, int3
   const int64_t c = decode_chunk(d, B, max_kv_len, num_splits);
   const int64_t ns = ((int64_t)max_kv_len + c - 1) / c;
   const size_t ph = (size_t)B * d->num_q_heads;
-  return align256(ph * ns * d->head_dim * sizeof(float)) + align256(ph * ns * sizeof(float));
+  const size_t pg = (size_t)B * d->num_kv_heads;
+  return align256(ph * ns * d->head_dim * sizeof(float)) + 2 * align256(ph * ns * sizeof(float)) +
+         align256(pg * ns * sizeof(int));
 }
 
 g4attn_status g4attn_decode(const g4attn_layer_desc* d, const g4attn_bf16* q,
@@ -232,8 +234,14 @@ g4attn_status g4attn_decode(const g4attn_layer_desc* d, const g4attn_bf16* q,
   const size_t ph = (size_t)B * d->num_q_heads;
   g4attn::DecodeArgs a{};
   a.q = q; a.kc = k_cache; a.vc = v_cache; a.kv_len = kv_len; a.out = out; a.lse = lse;
-  a.o_part = (float*)workspace;
-  a.lse_part = (float*)((char*)workspace + align256(ph * ns * d->head_dim * sizeof(float)));
+  char* wsp = (char*)workspace;
+  a.o_part = (float*)wsp;
+  wsp += align256(ph * ns * d->head_dim * sizeof(float));
+  a.lse_part = (float*)wsp;
+  wsp += align256(ph * ns * sizeof(float));
+  a.dmax = (float*)wsp;
+  wsp += align256(ph * ns * sizeof(float));
+  a.dflags = (int*)wsp;
   a.B = B; a.Hq = d->num_q_heads; a.Hkv = d->num_kv_heads; a.D = d->head_dim; a.cap = cache_cap;
   a.nsplit = (int)ns; a.chunk = (int)c; a.max_len = max_kv_len;
   a.scale_log2 = d->scale * g4attn::kLog2e;

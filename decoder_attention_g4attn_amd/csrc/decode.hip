@@ -10,8 +10,10 @@
 // when the value cache is the key cache (one tensor for both), one LDS tile
 // feeds both products.
 //
-// Per wave: 16-row tiles, double-buffered in the wave's own LDS region with
-// direct global->LDS loads (no workgroup barrier in the loop).
+// Per wave: 16-row tiles streamed through a ring of NS stages in the wave's
+// own LDS region with direct global->LDS loads, NS-1 tiles in flight (no
+// workgroup barrier in the loop; the wait for the oldest tile is an exact
+// vector-memory count).
 //   S^T[16 keys x 16 heads] = K Q^T      v_mfma_f32_16x16x32_bf16
 //   O^T[16 dims x 16 heads] += V^T P^T   v_mfma_f32_16x16x16_bf16, with V^T
 //                                         fed by the transposing LDS read
@@ -39,10 +41,15 @@ template <int D, bool SAME_KV>
 struct DCfg {
   static constexpr int TILE = (D == 512 ? 16 : 8) * kSegD;
   static constexpr int STAGE = TILE * (SAME_KV ? 1 : 2);
+  // 4 waves x 2 stages (K=V) measured faster than 2 x 4 or 3 x 3 at the same
+  // LDS size: more independent waves keep more loads in flight.
   static constexpr int WAVES = SAME_KV ? 4 : 2;
+  static constexpr int NS = 2;                              // ring stages per wave
+  static constexpr int LPT = (SAME_KV ? 1 : 2) * (D == 512 ? 16 : 8);  // loads per tile
   static constexpr int NT = D / 32;  // QK^T k-steps
   static constexpr int NC = D / 16;  // PV dim blocks
 };
+
 
 template <int D>
 __device__ __forceinline__ void load_rows(const uint16_t* base, int row0, int nrows, char* tile, int lane) {
@@ -68,13 +75,20 @@ __device__ __forceinline__ void load_rows(const uint16_t* base, int row0, int nr
   }
 }
 
-template <int D, bool SAME_KV>
-__global__ __launch_bounds__((SAME_KV ? 4 : 2) * 64) void decode_split_kernel(DecodeArgs a) {
+// Softmax per chunk with a fixed reference, as in the prefill kernel: each
+// wave's reference for a head is that head's maximum over the wave's first
+// tile; P = exp2(s - m_ref) is accumulated without rescaling O.  A chunk whose
+// true maximum ends more than kHeadroom above a reference is flagged and
+// recomputed by the REDO launch with the true maxima (every P <= 1 then).
+constexpr float kHeadroom = 64.f;
+
+template <int D, bool SAME_KV, bool REDO>
+__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   typedef DCfg<D, SAME_KV> C;
-  __shared__ __attribute__((aligned(1024))) char smem[C::WAVES * 2 * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[C::WAVES * C::NS * C::STAGE];
   __shared__ float s_m[C::WAVES][16], s_l[C::WAVES][16];
 
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = a.Hq / a.Hkv;
@@ -83,11 +97,13 @@ __global__ __launch_bounds__((SAME_KV ? 4 : 2) * 64) void decode_split_kernel(De
   if (r0 >= n) return;  // beyond this sequence: the combine never reads it
   const int r1 = min(r0 + a.chunk, n);
   const int ntile = (r1 - r0 + kRows - 1) / kRows;
+  const int64_t blk = ((int64_t)b * a.Hkv + g) * a.nsplit + split;
+  if (REDO && a.dflags[blk] == 0) return;
 
   const int64_t slice = ((int64_t)b * a.Hkv + g) * a.cap * D;
   const uint16_t* kbase = a.kc + slice;
   const uint16_t* vbase = a.vc + slice;
-  char* mybuf = smem + wave * 2 * C::STAGE;
+  char* mybuf = smem + wave * C::NS * C::STAGE;
 
   // Q^T (B operand of the 16x16x32 MFMA): lane -> head (lane & 15), dims 32t + 8(lane >> 4) ..
   const int hcol = lane & 15, kq = lane >> 4;
@@ -105,7 +121,9 @@ __global__ __launch_bounds__((SAME_KV ? 4 : 2) * 64) void decode_split_kernel(De
   f32x4 oacc[C::NC];
 #pragma unroll
   for (int c = 0; c < C::NC; ++c) oacc[c] = f32x4{};
-  float m_run = -INFINITY, l_part = 0.f;
+  float m_ref = -INFINITY, m_true = -INFINITY, l_part = 0.f;
+  const int64_t hrow = ((int64_t)b * a.Hq + g * G + (hvalid ? hcol : 0)) * a.nsplit + split;
+  if (REDO) m_ref = a.dmax[hrow];
 
   const int k_rowoff = d_row_off<D>(lane & 15), k_x = d_xor(lane & 15);
   // transposing read: issuing lane feeds row 4*(lane>>4) + ((lane>>2)&3), dims 16cb + 4*(lane&3)
@@ -114,21 +132,34 @@ __global__ __launch_bounds__((SAME_KV ? 4 : 2) * 64) void decode_split_kernel(De
   const int tr_off = d_row_off<D>(tR) + (tq & 1) * 8;
   const int tr_j = (tq >> 1) ^ d_xor(tR);
 
-  int it = 0;
-  int tl = wave;
-  if (tl < ntile) {
-    load_rows<D>(kbase, r0 + tl * kRows, r1, mybuf, lane);
-    if (!SAME_KV) load_rows<D>(vbase, r0 + tl * kRows, r1, mybuf + C::TILE, lane);
-  }
-  for (; tl < ntile; tl += C::WAVES, ++it) {
-    wait_vmem_all();  // this tile has landed (only this wave's loads are in flight)
-    char* cur = mybuf + (it & 1) * C::STAGE;
-    const int nx = tl + C::WAVES;
-    if (nx < ntile) {
-      char* nxt = mybuf + ((it + 1) & 1) * C::STAGE;
-      load_rows<D>(kbase, r0 + nx * kRows, r1, nxt, lane);
-      if (!SAME_KV) load_rows<D>(vbase, r0 + nx * kRows, r1, nxt + C::TILE, lane);
+  // tiles of this wave: tl = wave + WAVES * it
+  const int nmine = ntile > wave ? (ntile - wave + C::WAVES - 1) / C::WAVES : 0;
+  auto issue = [&](int it) {
+    const int tl = wave + C::WAVES * it;
+    char* st = mybuf + (it % C::NS) * C::STAGE;
+    load_rows<D>(kbase, r0 + tl * kRows, r1, st, lane);
+    if (!SAME_KV) load_rows<D>(vbase, r0 + tl * kRows, r1, st + C::TILE, lane);
+  };
+#pragma unroll
+  for (int it = 0; it < C::NS - 1; ++it)
+    if (it < nmine) issue(it);
+  for (int it = 0; it < nmine; ++it) {
+    if constexpr (C::NS == 1) issue(it);  // no ring: other waves hide the latency
+    // wait for tile it; tiles it+1 .. it+NS-2 (if any) may stay in flight
+    const int newer = min(nmine - 1 - it, C::NS - 2);
+    if constexpr (C::NS >= 4) {
+      if (newer >= 2) wait_vmem<2 * C::LPT>();
+      else if (newer == 1) wait_vmem<C::LPT>();
+      else wait_vmem<0>();
+    } else if constexpr (C::NS == 3) {
+      if (newer >= 1) wait_vmem<C::LPT>();
+      else wait_vmem<0>();
+    } else {
+      wait_vmem<0>();
     }
+    if (C::NS > 1 && it + C::NS - 1 < nmine) issue(it + C::NS - 1);  // into the stage tile it-1 used
+    const int tl = wave + C::WAVES * it;
+    char* cur = mybuf + (it % C::NS) * C::STAGE;
 
     f32x4 sacc = f32x4{};
 #pragma unroll
@@ -143,20 +174,14 @@ __global__ __launch_bounds__((SAME_KV ? 4 : 2) * 64) void decode_split_kernel(De
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[i] = (key0 + i < r1) ? sacc[i] * a.scale_log2 : -INFINITY;
     float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
-    float p[4], ps = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { p[i] = __builtin_amdgcn_exp2f(s[i] - m_use); ps += p[i]; }
-    l_part = l_part * alpha + ps;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-      for (int c = 0; c < C::NC; ++c) oacc[c] *= alpha;
+    m_true = fmaxf(m_true, mx);
+    if (!REDO && it == 0) {  // the wave's first tile fixes its reference
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      m_ref = fmaxf(mx, __shfl_xor(mx, 32, 64));
     }
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { p[i] = __builtin_amdgcn_exp2f(s[i] - m_ref); l_part += p[i]; }
     const u32x2 pw = {pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3])};
     const i16x4_t pb = __builtin_bit_cast(i16x4_t, pw);
     const char* vt = SAME_KV ? cur : cur + C::TILE;
@@ -167,10 +192,15 @@ __global__ __launch_bounds__((SAME_KV ? 4 : 2) * 64) void decode_split_kernel(De
     }
   }
 
-  // ---- merge the waves' partial states
+  // ---- merge the waves' partial states (each relative to its own reference)
   float l_tot = l_part + __shfl_xor(l_part, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
-  if (lane < 16) { s_m[wave][lane] = m_run; s_l[wave][lane] = l_tot; }
+  float mt = fmaxf(m_true, __shfl_xor(m_true, 16, 64));
+  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+  __shared__ float s_t[C::WAVES][16];
+  __shared__ int s_over[C::WAVES];
+  if (lane < 16) { s_m[wave][lane] = m_ref; s_l[wave][lane] = l_tot; s_t[wave][lane] = mt; }
+  if (lane == 0) s_over[wave] = __builtin_amdgcn_ballot_w64(hvalid && mt > m_ref + kHeadroom) != 0;
   __syncthreads();  // all waves are done with their tiles; reuse LDS for O
   float* so = (float*)smem;  // [WAVES][16 heads][D]
   if (hvalid) {
@@ -178,6 +208,18 @@ __global__ __launch_bounds__((SAME_KV ? 4 : 2) * 64) void decode_split_kernel(De
     for (int c = 0; c < C::NC; ++c)
 #pragma unroll
       for (int i = 0; i < 4; ++i) so[(wave * 16 + hcol) * D + 16 * c + 4 * kq + i] = oacc[c][i];
+  }
+  if (!REDO && threadIdx.x == 0) {
+    int over = 0;
+#pragma unroll
+    for (int w = 0; w < C::WAVES; ++w) over |= s_over[w];
+    a.dflags[blk] = over;
+  }
+  if (!REDO && threadIdx.x < G) {
+    float t = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < C::WAVES; ++w) t = fmaxf(t, s_t[w][threadIdx.x]);
+    a.dmax[((int64_t)b * a.Hq + g * G + threadIdx.x) * a.nsplit + split] = t;
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < G * D; idx += C::WAVES * 64) {
@@ -226,8 +268,12 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 template <int D, bool SAME>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t st) {
   typedef DCfg<D, SAME> C;
-  hipLaunchKernelGGL((decode_split_kernel<D, SAME>), dim3(a.nsplit, a.Hkv, a.B), dim3(C::WAVES * 64), 0, st, a);
+  const dim3 grid(a.nsplit, a.Hkv, a.B);
+  hipLaunchKernelGGL((decode_split_kernel<D, SAME, false>), grid, dim3(C::WAVES * 64), 0, st, a);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_split_kernel<D, SAME, true>), grid, dim3(C::WAVES * 64), 0, st, a);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.Hq, a.B), dim3(256), 0, st, a);
   return hipGetLastError();

@@ -40,10 +40,23 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// One 16-byte-per-lane direct global->LDS copy: lane i's 16 bytes land at
-// lds_base + 16*i (lds_base must be wave-uniform).
+// Direct global->LDS copies: lane i's 16 (or 4) bytes land at lds_base +
+// 16*i (4*i); lds_base must be wave-uniform.  They are issued as inline
+// assembly on purpose: the compiler then does not know these loads write LDS
+// and does not drain every one of them before each transposing LDS read.
+// Callers therefore order them explicitly: `s_waitcnt vmcnt` (wait_vmem*)
+// before any read of the data, and a workgroup barrier before a buffer is
+// reused.  The instruction has no register results.
+__device__ __forceinline__ uint32_t lds_addr(const G4_LDS void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
 __device__ __forceinline__ void g2lds16(const void* gptr, G4_LDS void* lds_base) {
-  __builtin_amdgcn_global_load_lds(gptr, lds_base, 16, 0, 0);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr(lds_base))
+               : "memory", "m0");
+}
+__device__ __forceinline__ void g2lds4(const void* gptr, G4_LDS void* lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(lds_addr(lds_base))
+               : "memory", "m0");
 }
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const G4_LDS char* p) {
@@ -60,6 +73,12 @@ __device__ __forceinline__ bf16x8 cat_tr(i16x4 a, i16x4 b) {
 }
 
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt vmcnt(n): n must be a compile-time constant.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 }  // namespace g4attn
 
@@ -117,6 +136,8 @@ struct DecodeArgs {
   float* lse;               // [B, Hq] or NULL
   float* o_part;            // [B, Hq, nsplit, D]
   float* lse_part;          // [B, Hq, nsplit]
+  float* dmax;              // [B, Hq, nsplit] true logit maxima (log2 domain) of each chunk
+  int* dflags;              // [B, Hkv, nsplit] reference-overflow flags of each chunk
   int B, Hq, Hkv, D, cap, nsplit, chunk;
   int max_len;              // host bound; kv_len values are clamped to [0, max_len]
   float scale_log2;

@@ -119,8 +119,8 @@ __device__ __forceinline__ void load_tile(const PrefillArgs& a, char* stage, int
     }
     if (wave == 0) {
       const int key = min(key0 + (lane & 31), a.S - 1);
-      __builtin_amdgcn_global_load_lds((const char*)(a.r + rowbase + kfirst) + (uint32_t)(key - kfirst) * 4u,
-                                       (G4_LDS void*)(stage + C::R_OFF), 4, 0, 0);
+      g2lds4((const char*)(a.r + rowbase + kfirst) + (uint32_t)(key - kfirst) * 4u,
+             (G4_LDS void*)(stage + C::R_OFF));
     }
   }
 }
@@ -221,7 +221,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   if (REDO) m_ref = valid ? a.mrow[mrow_idx] : 0.f;
 
   for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-    __syncthreads();  // tile kt has landed in LDS; every wave is done with tile kt-1
+    wait_vmem_all();  // this wave's copies of tile kt have landed
+    __syncthreads();  // all of tile kt is in LDS; every wave is done with tile kt-1
     const int so = ((kt - kt_lo) & 1) * C::STAGE;
     const G4_LDS char* cur = (const G4_LDS char*)smem + so;
     if (kt < kt_hi) load_tile<D, TIED>(a, smem + (C::STAGE - so), kt + 1, b, g, wave, lane);

@@ -108,7 +108,8 @@ def test_decode_workspace_sizes():
         w = g4.g4attn_decode_workspace_bytes(d, 2, 1000, splits)
         chunk = -(-(-(-1000 // splits)) // 64) * 64
         ns = -(-1000 // chunk)
-        assert w == -(-2 * 32 * ns * 512 * 4 // 256) * 256 + -(-2 * 32 * ns * 4 // 256) * 256
+        a256 = lambda x: -(-x // 256) * 256
+        assert w == a256(2 * 32 * ns * 512 * 4) + 2 * a256(2 * 32 * ns * 4) + a256(2 * 4 * ns * 4)
 
 
 def test_norm_rope_validation():

@@ -302,3 +302,26 @@ def test_prefill_reference_overflow_redo(gpu_lib, D, w, kv_tied):
     torch.cuda.synchronize()
     assert_parity(f64(out), ro, f"redo D={D} w={w} tied={kv_tied}")
     np.testing.assert_allclose(lse.cpu().numpy(), rl, rtol=1e-4, atol=2e-3)
+
+
+@pytest.mark.parametrize("same", [True, False])
+def test_decode_reference_overflow_redo(gpu_lib, same):
+    """Logits growing along the cache (coordinate 0 = j/2048, q_0 = 2560) rise
+    by ~200 within one chunk, forcing the decode recomputation pass."""
+    g4 = gpu_lib
+    B, Hq, Hkv, D, n = 2, 8, 1, 512, 4000
+    q = torch.zeros((B, Hq, D), dtype=torch.bfloat16, device=DEV)
+    q[..., 0] = 2560.0
+    kc = _bf((B, Hkv, n, D), 91)
+    kc[:, :, :, 0] = (torch.arange(n, device=DEV, dtype=torch.float32) / 2048).to(torch.bfloat16)
+    vc = kc if same else _bf((B, Hkv, n, D), 92)
+    kv_len = torch.tensor([n, n - 1000], dtype=torch.int32, device=DEV)
+    desc = g4.layer_desc(Hq, Hkv, D)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=DEV)
+    g4.g4attn_decode(desc, q, kc, vc, kv_len, n, out, lse=lse, num_splits=1)
+    torch.cuda.synchronize()
+    k64 = f64(kc)
+    ro, rl = oat.decode_attention(f64(q), k64, k64 if same else f64(vc), kv_len.cpu().numpy(), desc.scale)
+    assert_parity(f64(out), ro, f"decode redo same={same}")
+    np.testing.assert_allclose(lse.cpu().numpy(), rl, rtol=1e-5, atol=2e-3)
