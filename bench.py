@@ -42,7 +42,22 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["sliding", "global", "decode"], default=None,
                     help="time one stage only (profiling aid)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB device-to-device copy 3 times (HBM-counter calibration)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain copy of known size: 1 GiB read + 1 GiB written per launch."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read_per_launch": n, "copy_bytes_written_per_launch": n, "launches": 3}))
 
 
 class Stage:
@@ -179,6 +194,9 @@ def cpu_baseline(torch, gen, st, budget_s=15.0):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the attention path shards by KV head / batch without collectives).", file=sys.stderr)
@@ -189,7 +207,10 @@ def main():
 
     g4.load()
     torch.cuda.set_device(0)
+    log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)
+    log("generating inputs")
     st = build_workloads(torch, g4, gen, WORKLOADS)
+    log("inputs ready")
 
     plan = [("sliding_prologue", run_sliding, "sliding"), ("sliding_attn", run_sliding_attn, "sliding"),
             ("global_prologue", run_global_pro, "global"), ("global_attn", run_global_attn, "global"),
@@ -214,12 +235,14 @@ def main():
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
     all_evs = []
     t0 = time.perf_counter()
     for _ in range(args.steps):
         all_evs.append(step(True))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    log(f"timed {args.steps} steps in {wall:.2f}s")
     ms = {}
     for evs in all_evs:
         for name, e0, e1 in evs:
@@ -273,6 +296,7 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu_baseline and "global_attn" in avg:
+        log("timing the CPU oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(torch, gen, st)
     print(json.dumps(out))
 
