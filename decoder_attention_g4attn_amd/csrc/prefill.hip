@@ -125,6 +125,37 @@ __device__ __forceinline__ void load_tile(const PrefillArgs& a, char* stage, int
   }
 }
 
+// Workgroup -> (batch b, KV group g, row tile) for the 8 XCDs of the chip.
+// The dispatcher hands linear workgroup ids to the XCDs round-robin, and
+// each XCD has its own L2.  With NG = B*Hkv groups of T tiles:
+//   NG % 8 == 0          : each XCD takes NG/8 whole groups;
+//   8 % NG == 0, T % (8/NG) == 0 : each group is spread over 8/NG XCDs, XCD
+//                          c taking every (8/NG)-th tile in weight order;
+//   otherwise            : plain order.
+// so an XCD's L2 serves one group's keys instead of every group's, work
+// per XCD stays balanced, and each XCD runs its heaviest (latest) tiles first.
+__device__ __forceinline__ void wg_map(int T, int Hkv, int& b, int& g, int& tile) {
+  constexpr int X = 8;
+  const int NG = Hkv * (int)gridDim.z;
+  const int L = (int)blockIdx.x + T * ((int)blockIdx.y + Hkv * (int)blockIdx.z);
+  int grp, r;
+  if (NG % X == 0) {
+    const int xcd = L % X, k = L / X;
+    grp = xcd * (NG / X) + k / T;
+    r = k % T;
+  } else if (X % NG == 0 && T % (X / NG) == 0) {
+    const int m = X / NG, xcd = L % X, k = L / X;
+    grp = xcd / m;
+    r = k * m + xcd % m;
+  } else {
+    grp = (int)blockIdx.y + Hkv * (int)blockIdx.z;
+    r = (int)blockIdx.x;
+  }
+  g = grp % Hkv;
+  b = grp / Hkv;
+  tile = T - 1 - r;  // heaviest (latest) rows first
+}
+
 // Scheduling-group masks (LLVM AMDGPU): MFMA, LDS read.
 constexpr int kSgMfma = 0x008;
 constexpr int kSgDsRead = 0x100;
@@ -142,10 +173,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const int hh = lane >> 5;   // lane half
   const int lr = lane & 31;   // row within the wave
   const int G = a.Hq / a.Hkv;
-  const int b = blockIdx.z;
-  const int g = blockIdx.y;
   const int ntiles = (int)(((int64_t)a.S * G + kBM - 1) / kBM);
-  const int tile = ntiles - 1 - (int)blockIdx.x;  // heaviest (latest) rows first
+  int b, g, tile;
+  wg_map(ntiles, a.Hkv, b, g, tile);
 
   const int64_t F0 = (int64_t)tile * kBM;
   const int64_t Flast = min(F0 + kBM - 1, (int64_t)a.S * G - 1);
