@@ -19,19 +19,31 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest even, NaN kept quiet: one v_cvt_pk_bf16_f32
+// (gfx950) converts a pair.
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-  return f2bf(lo) | (f2bf(hi) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
+__device__ __forceinline__ uint32_t f2bf(float f) { return pack_bf2(f, 0.f) & 0xffffu; }
 __device__ __forceinline__ float bf2f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// max / sum of a value and its copy in lane l ^ 32 (v_permlane32_swap: each
+// result holds the lane's own value in one output and the partner's in the
+// other, so combining both outputs needs no lane select).
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Wave-wide (64 lanes) reductions.
 __device__ __forceinline__ float wave_sum(float v) {

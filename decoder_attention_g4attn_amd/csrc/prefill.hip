@@ -388,8 +388,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)ntiles, (unsigned)a.Hkv, (unsigned)a.B);
   for (int redo = 0; redo < 2; ++redo) {
     if (a.kv_tied)
-      hipLaunchKernelGGL((redo ? prefill_kernel<512, true, true> : prefill_kernel<512, true, false>), grid,
-                         dim3(256), 0, st, a);
+      hipLaunchKernelGGL((redo ? prefill_kernel<512, true, true> : prefill_kernel<512, true, false>),
+                         grid, dim3(256), 0, st, a);
     else if (a.D == 512)
       hipLaunchKernelGGL((redo ? prefill_kernel<512, false, true> : prefill_kernel<512, false, false>), grid,
                          dim3(256), 0, st, a);
