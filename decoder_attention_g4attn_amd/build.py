@@ -52,7 +52,13 @@ def _compile(src, verbose):
     return obj
 
 
+def generate():
+    """Regenerate the assembly include of the prefill kernel (no-op if unchanged)."""
+    subprocess.run([sys.executable, os.path.join(CSRC, "gen_qk_asm.py")], check=True)
+
+
 def build(verbose=False):
+    generate()
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=4) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), sources()))

@@ -121,19 +121,18 @@ g4attn_status g4attn_norm_rope(const g4attn_bf16* x, g4attn_bf16* y, const g4att
   return hip_status(g4attn::launch_norm_rope(a, (hipStream_t)stream));
 }
 
-// Prefill workspace: per-row maxima + per-wave flags (all layers), then the
-// K=V inverse RMS and rotated slice.
+// Prefill workspace: per-wave reference-overflow flags (all layers), then
+// the K=V per-key factor and rotated slice.
 struct PrefillWs {
-  size_t mrow, flags, r, krot, total;
+  size_t flags, r, krot, total;
 };
 static PrefillWs prefill_ws(const g4attn_layer_desc* d, int32_t B, int32_t S) {
   PrefillWs w{};
   const int64_t G = d->num_q_heads / d->num_kv_heads;
   const int64_t ntiles = ((int64_t)S * G + 127) / 128;
   const size_t rows = (size_t)B * d->num_kv_heads * S;
-  w.mrow = 0;
-  w.flags = align256((size_t)B * d->num_q_heads * S * sizeof(float));
-  w.r = w.flags + align256((size_t)B * d->num_kv_heads * ntiles * 4 * sizeof(int));
+  w.flags = 0;
+  w.r = align256((size_t)B * d->num_kv_heads * ntiles * 4 * sizeof(int));
   w.krot = w.r + (d->k_eq_v ? align256(rows * sizeof(float)) : 0);
   w.total = w.krot + (d->k_eq_v ? align256(rows * 128 * sizeof(uint16_t)) : 0);
   return w;
@@ -159,6 +158,7 @@ g4attn_status g4attn_prefill(const g4attn_layer_desc* d, const g4attn_bf16* q,
     if (!w_k) return G4ATTN_ERR_NULL;
     if (v) return G4ATTN_ERR_SHAPE;  // K=V takes one tensor
     if (d->head_dim != 512 || d->rotary_dims != 128) return G4ATTN_ERR_UNSUPPORTED;
+    if (!(fabsf(d->scale) <= 0x1p30f)) return G4ATTN_ERR_UNSUPPORTED;
   } else if (!v) {
     return G4ATTN_ERR_NULL;
   }
@@ -176,10 +176,15 @@ g4attn_status g4attn_prefill(const g4attn_layer_desc* d, const g4attn_bf16* q,
   a.B = B; a.S = S; a.Hq = d->num_q_heads; a.Hkv = d->num_kv_heads; a.D = d->head_dim;
   a.window = d->window; a.kv_tied = d->k_eq_v;
   a.scale_log2 = d->scale * g4attn::kLog2e;
+  // K=V: the logit scale rides on the per-key factor r (and is divided out of
+  // the output) unless it is too small for that, when it scales the queries.
+  const float c = a.scale_log2;
+  const bool fold = fabsf(c) >= 0x1p-30f;
+  a.qmul = fold ? 1.f : c;
+  a.omul = fold ? 1.f / c : 1.f;
   for (int i = 0; i < 3; ++i) { a.qs[i] = q_strides[i]; a.ks[i] = kv_strides[i]; a.os[i] = o_strides[i]; }
   hipStream_t s = (hipStream_t)stream;
   char* wsp = (char*)workspace;
-  a.mrow = (float*)(wsp + ws.mrow);
   a.flags = (int*)(wsp + ws.flags);
   if (d->k_eq_v) {
     float* r = (float*)(wsp + ws.r);
@@ -189,6 +194,7 @@ g4attn_status g4attn_prefill(const g4attn_layer_desc* d, const g4attn_bf16* q,
     p.B = B; p.S = S; p.Hkv = d->num_kv_heads; p.rot = d->rotary_dims;
     p.log2_theta = log2((double)d->rope_theta);
     p.eps = d->rms_eps;
+    p.rscale = fold ? c : 1.f;
     for (int i = 0; i < 3; ++i) p.xs[i] = kv_strides[i];
     st = hip_status(g4attn::launch_kv_prep(p, s));
     if (st != G4ATTN_OK) return st;

@@ -71,6 +71,20 @@ __device__ __forceinline__ void g2lds4(const void* gptr, G4_LDS void* lds_base) 
                : "memory", "m0");
 }
 
+// The same copies with a wave-uniform 64-bit base in scalar registers plus
+// an unsigned 32-bit per-lane byte offset (the scalar-base form); `lds` is the
+// wave-uniform LDS byte address of lane 0's destination.
+__device__ __forceinline__ void g2lds16s(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+__device__ __forceinline__ void g2lds4s(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ bf16x8 lds_read_b128(const G4_LDS char* p) {
   return *(const G4_LDS bf16x8*)p;
 }
@@ -113,9 +127,10 @@ hipError_t launch_norm_rope(const NormRopeArgs& a, hipStream_t st);
 struct KvPrepArgs {         // K=V prefill pre-pass
   const uint16_t* x;        // [B, S, Hkv, 512] strided
   const uint16_t* w_k;      // [512]
-  float* r;                 // [B, Hkv, S]
+  float* r;                 // [B, Hkv, S] inverse RMS of each row times rscale
   uint16_t* krot;           // [B, Hkv, S, 128]
   int B, S, Hkv, rot;
+  float rscale;
   double log2_theta;
   float eps;
   int64_t xs[3];
@@ -127,14 +142,14 @@ struct PrefillArgs {
   const uint16_t* k;        // K, or X (K=V)
   const uint16_t* v;        // V (NULL for K=V)
   const uint16_t* w_k;      // K=V only
-  const float* r;           // K=V only: [B, Hkv, S]
+  const float* r;           // K=V only: [B, Hkv, S] inverse RMS of each key row times scale_log2
   const uint16_t* krot;     // K=V only: [B, Hkv, S, 128]
-  float* mrow;              // [B, Hq, S] true row maxima (log2 domain), written by the main pass
   int* flags;               // [B, Hkv, ntiles, 4] per-wave reference-overflow flags
   uint16_t* out;
   float* lse;
   int B, S, Hq, Hkv, D, window, kv_tied;
   float scale_log2;         // scale * log2(e)
+  float qmul, omul;         // K=V only: query and output multipliers (see g4attn_prefill)
   int64_t qs[3], ks[3], os[3];
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);

@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(KvPrepArgs a) {
     for (int e = 0; e < E; ++e) ss += lo[e] * lo[e] + hi[e] * hi[e];
     ss = wave_sum(ss);
     const int64_t row = ((int64_t)b * a.Hkv + g) * a.S + t;
-    if (lane == 0) a.r[row] = 1.0f / sqrtf(ss / (float)D + a.eps);
+    if (lane == 0) a.r[row] = a.rscale / sqrtf(ss / (float)D + a.eps);
     if (rot_lane) {
       float ylo[E], yhi[E];
 #pragma unroll

@@ -31,6 +31,7 @@
 // distinct bank groups, and the transposing-read addresses stay affine in
 // the dim block.
 #include "g4attn_internal.h"
+#include "prefill_qk_asm.inc"
 
 namespace g4attn {
 namespace {
@@ -66,63 +67,68 @@ __device__ __forceinline__ int kr_xor(int R) { return (R >> 2) & 3; }
 // Is the 16-dim k-step t one of the rotated (Krot) dims 0..63 / 256..319?
 __device__ __forceinline__ constexpr bool rot_step(int t) { return t < 4 || (t >= 16 && t < 20); }
 
-// Global->LDS copy of key tile kt.  Each row's base address is wave-uniform
-// (scalar registers) and lanes add an unsigned 32-bit byte offset, which maps
-// onto the scalar-base form of the load.
-template <int D, bool TIED>
-__device__ __forceinline__ void load_tile(const PrefillArgs& a, char* stage, int kt, int b, int g,
-                                          int wave, int lane) {
+// Global->LDS copy of key tile kt.  The tile's base address is wave-uniform
+// (scalar registers) and each lane adds an unsigned 32-bit byte offset (the
+// scalar-base form of the load).  FULL: all 32 keys are < S; otherwise rows
+// past S re-read row S-1 (they are masked).
+template <int D, bool TIED, bool FULL>
+__device__ __forceinline__ void load_tile_rows(const PrefillArgs& a, uint32_t stage, int kt, int b, int g,
+                                               int wave, int lane) {
   typedef Cfg<D, TIED> C;
   const int key0 = kt * kBN;
-  const int64_t kb = b * a.ks[0] + g * a.ks[2];
-  auto row_base = [&](const uint16_t* base, int R) {
-    int key = key0 + R;
-    key = key < a.S ? key : a.S - 1;  // rows past S are masked; stay in bounds
-    return (const char*)(base + kb + key * a.ks[1]);
-  };
+  const int last = a.S - 1 - key0;  // last in-range row of the tile
+  const int64_t rs = a.ks[1] * 2;   // key stride in bytes
+  auto row_off = [&](int R) -> int64_t { return (int64_t)(FULL ? R : min(R, last)) * rs; };
+  const int64_t tb = (b * a.ks[0] + g * a.ks[2] + (int64_t)key0 * a.ks[1]) * 2;
   const int ntile = TIED ? 1 : 2;
 #pragma unroll
   for (int which = 0; which < ntile; ++which) {
-    const uint16_t* src = which == 0 ? a.k : a.v;
-    char* tile = stage + which * C::KT_BYTES;
+    const char* src = (const char*)(which == 0 ? a.k : a.v) + tb;
+    const uint32_t tile = stage + which * C::KT_BYTES;
     if (D == 512) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int R = wave * 8 + i;
         const uint32_t off = (uint32_t)(lane ^ kv_xor<D>(R)) * 16u;
-        g2lds16(row_base(src, R) + off, (G4_LDS void*)(tile + kv_row_off<D>(R)));
+        g2lds16s(src + row_off(R), off, tile + kv_row_off<D>(R));
       }
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        // lanes 0..31 copy row s, lanes 32..63 row s + 16 (rows are clamped
-        // independently, so the second row's offset is measured from the first)
+        // lanes 0..31 copy row s, lanes 32..63 row s + 16
         const int s = wave * 4 + i;
-        const char* b0 = row_base(src, s);
-        const uint32_t d = (uint32_t)(row_base(src, s + 16) - b0);
+        const uint32_t d = (uint32_t)(row_off(s + 16) - row_off(s));
         const uint32_t off = (lane >> 5) * d + (uint32_t)((lane & 31) ^ kv_xor<D>(s)) * 16u;
-        g2lds16(b0 + off, (G4_LDS void*)(tile + s * kSeg));
+        g2lds16s(src + row_off(s), off, tile + s * kSeg);
       }
     }
   }
   if (TIED) {
-    const int64_t rowbase = ((int64_t)b * a.Hkv + g) * a.S;
-    const int kfirst = min(key0, a.S - 1);
+    const int64_t row0 = ((int64_t)b * a.Hkv + g) * a.S + key0;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int s = wave * 2 + i;
       // lanes 16q .. 16q+15 copy Krot row s + 8q
       const int R = s + 8 * (lane >> 4);
-      const int key = min(key0 + R, a.S - 1);
-      const uint32_t off = (uint32_t)(key - kfirst) * 256u + (uint32_t)((lane & 15) ^ kr_xor(R)) * 16u;
-      g2lds16((const char*)(a.krot + (rowbase + kfirst) * 128) + off, (G4_LDS void*)(stage + C::KR_OFF + s * kSeg));
+      const int Re = FULL ? R : min(R, last);
+      const uint32_t off = (uint32_t)Re * 256u + (uint32_t)((lane & 15) ^ kr_xor(R)) * 16u;
+      g2lds16s(a.krot + row0 * 128, off, stage + C::KR_OFF + s * kSeg);
     }
     if (wave == 0) {
-      const int key = min(key0 + (lane & 31), a.S - 1);
-      g2lds4((const char*)(a.r + rowbase + kfirst) + (uint32_t)(key - kfirst) * 4u,
-             (G4_LDS void*)(stage + C::R_OFF));
+      const int R = lane & 31;
+      const int Re = FULL ? R : min(R, last);
+      g2lds4s(a.r + row0, (uint32_t)Re * 4u, stage + C::R_OFF);
     }
   }
+}
+
+template <int D, bool TIED>
+__device__ __forceinline__ void load_tile(const PrefillArgs& a, uint32_t stage, int kt, int b, int g,
+                                          int wave, int lane) {
+  if (kt * kBN + kBN <= a.S)
+    load_tile_rows<D, TIED, true>(a, stage, kt, b, g, wave, lane);
+  else
+    load_tile_rows<D, TIED, false>(a, stage, kt, b, g, wave, lane);
 }
 
 // Workgroup -> (batch b, KV group g, row tile) for the 8 XCDs of the chip.
@@ -159,15 +165,38 @@ __device__ __forceinline__ void wg_map(int T, int Hkv, int& b, int& g, int& tile
 // Scheduling-group masks (LLVM AMDGPU): MFMA, LDS read.
 constexpr int kSgMfma = 0x008;
 constexpr int kSgDsRead = 0x100;
-constexpr int kLook = 3;  // LDS operand reads issued ahead of their MFMA
+constexpr int kLook = 3;  // PV: LDS operand reads issued ahead of their MFMA
+
+// S^T (32 keys x 32 rows) = K Q^T of one LDS tile, as one assembly block
+// (prefill_qk_asm.inc) that leaves S^T in VGPRs and ends with every LDS read
+// complete and the MFMA result readable.  kb0/kb1 (kr0/kr1): LDS byte
+// addresses of this lane's K (Krot) chunks for even/odd k-steps.
+template <int D, bool TIED>
+__device__ __forceinline__ f32x16 qk_tile(const bf16x8 (&qf)[D / 16], uint32_t kb0, uint32_t kb1,
+                                          uint32_t kr0, uint32_t kr1) {
+  f32x16 s;
+  bf16x8 tmp[G4_QK_TEMPS];
+  if constexpr (TIED) {
+    asm volatile(G4_QK_ASM_512_TIED
+                 : G4_QK_OUTS
+                 : G4_QK_Q32, [kb0] "v"(kb0), [kb1] "v"(kb1), [kr0] "v"(kr0), [kr1] "v"(kr1)
+                 : "memory");
+  } else if constexpr (D == 512) {
+    asm volatile(G4_QK_ASM_512 : G4_QK_OUTS : G4_QK_Q32, [kb0] "v"(kb0), [kb1] "v"(kb1) : "memory");
+  } else {
+    asm volatile(G4_QK_ASM_256 : G4_QK_OUTS : G4_QK_Q16, [kb0] "v"(kb0), [kb1] "v"(kb1) : "memory");
+  }
+  return s;
+}
 
 // REDO = false: main pass.  REDO = true: recompute the workgroups whose main
-// pass flagged a reference overflow, with the row maxima the main pass found.
+// pass flagged a reference overflow, after a first sweep that finds each
+// row's true maximum.
 template <int D, bool TIED, bool REDO>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   typedef Cfg<D, TIED> C;
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE];
-
+  const uint32_t lds0 = lds_addr((G4_LDS void*)smem);  // LDS byte address of stage 0
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int hh = lane >> 5;   // lane half
@@ -193,12 +222,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   }
 
   // Prefetch the first tile, then load this lane's Q^T fragments (rows past S
-  // read row S-1; their results are never stored).
-  load_tile<D, TIED>(a, smem, kt_lo, b, g, wave, lane);
+  // read row S-1; their results are never stored).  K=V: the K-norm weight
+  // is folded into the non-rotated dims, times qmul.
+  load_tile<D, TIED>(a, lds0, kt_lo, b, g, wave, lane);
 
   bf16x8 qf[C::NT];
   {
     const uint16_t* qrow = a.q + b * a.qs[0] + (int64_t)min(tq, a.S - 1) * a.qs[1] + head * a.qs[2];
+    const bool qscale = TIED && a.qmul != 1.f;
 #pragma unroll
     for (int t = 0; t < C::NT; ++t) {
       const int d0 = 16 * t + 8 * hh;
@@ -207,7 +238,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         const u32x4 w = *(const u32x4*)(a.w_k + d0);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          raw[i] = pack_bf2(bf_lo(raw[i]) * bf_lo(w[i]), bf_hi(raw[i]) * bf_hi(w[i]));
+          raw[i] = pack_bf2(bf_lo(raw[i]) * bf_lo(w[i]) * a.qmul, bf_hi(raw[i]) * bf_hi(w[i]) * a.qmul);
+      } else if (qscale) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) raw[i] = pack_bf2(bf_lo(raw[i]) * a.qmul, bf_hi(raw[i]) * a.qmul);
       }
       qf[t] = __builtin_bit_cast(bf16x8, raw);
     }
@@ -217,10 +251,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   // 16t + 8hh ..): chunk (2t + hh) ^ x keeps t>>1 in the high bits, so the
   // address is koff[t & 1] + 64 (t >> 1).
   const int k_x = kv_xor<D>(lr), kr_x = kr_xor(lr);
-  const int koff0 = kv_row_off<D>(lr) + 16 * (hh ^ k_x);
-  const int koff1 = kv_row_off<D>(lr) + 16 * ((2 + hh) ^ k_x);
-  const int kroff0 = C::KR_OFF + kr_row_off(lr) + 16 * (hh ^ kr_x);
-  const int kroff1 = C::KR_OFF + kr_row_off(lr) + 16 * ((2 + hh) ^ kr_x);
+  const uint32_t koff0 = kv_row_off<D>(lr) + 16 * (hh ^ k_x);
+  const uint32_t koff1 = kv_row_off<D>(lr) + 16 * ((2 + hh) ^ k_x);
+  const uint32_t kroff0 = C::KR_OFF + kr_row_off(lr) + 16 * (hh ^ kr_x);
+  const uint32_t kroff1 = C::KR_OFF + kr_row_off(lr) + 16 * ((2 + hh) ^ kr_x);
   // PV operand (transposing read): issuing lane feeds row 16m + 8u + r0 of
   // dim block c at 64c + toff[m][u].
   const int tG = lane >> 4, te = (lane >> 2) & 3, tqd = lane & 3;
@@ -236,84 +270,100 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       toff[m][u] = vbase + kv_row_off<D>(R) + (tqd & 1) * 8 + 16 * (tr_chunk ^ kv_xor<D>(R));
     }
 
-  // Softmax with a fixed per-row reference: m_ref (log2 domain) is the row's
-  // maximum over its first tile with a visible key, and P = exp2(s - m_ref)
-  // is accumulated without ever rescaling O.  m_true tracks the real maximum;
-  // a wave whose rows end more than kHeadroom above m_ref flags its
-  // workgroup, which the REDO launch recomputes with m_ref = m_true (every
-  // P <= 1 then).
-  constexpr float kHeadroom = 64.f;
-  f32x16 oacc[C::NC];
-#pragma unroll
-  for (int c = 0; c < C::NC; ++c) oacc[c] = f32x16{};
-  float m_ref = -INFINITY, m_true = -INFINITY, l_part = 0.f;
-  const int64_t mrow_idx = ((int64_t)b * a.Hq + head) * a.S + tq;
-  if (REDO) m_ref = valid ? a.mrow[mrow_idx] : 0.f;
-
-  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-    wait_vmem_all();  // this wave's copies of tile kt have landed
-    __syncthreads();  // all of tile kt is in LDS; every wave is done with tile kt-1
-    const int so = ((kt - kt_lo) & 1) * C::STAGE;
-    const G4_LDS char* cur = (const G4_LDS char*)smem + so;
-    if (kt < kt_hi) load_tile<D, TIED>(a, smem + (C::STAGE - so), kt + 1, b, g, wave, lane);
-
-    // ---- S^T = K Q^T (32 keys x 32 rows), two accumulators, reads kLook ahead
-    auto kread = [&](int t) -> bf16x8 {
-      if (TIED && rot_step(t)) {  // Krot chunk 2u + hh, u = t (t < 4) or t - 12
-        const int u = t < 4 ? t : t - 12;
-        return lds_read_b128(cur + ((u & 1) ? kroff1 : kroff0) + 64 * (u >> 1));
-      }
-      return lds_read_b128(cur + ((t & 1) ? koff1 : koff0) + 64 * (t >> 1));
-    };
-    bf16x8 ka[kLook + 1];
-#pragma unroll
-    for (int t = 0; t < kLook; ++t) ka[t] = kread(t);
-    __builtin_amdgcn_sched_group_barrier(kSgDsRead, kLook, 0);
-    f32x16 s0 = f32x16{}, s1 = f32x16{};
-#pragma unroll
-    for (int t = 0; t < C::NT; ++t) {
-      if (t + kLook < C::NT) ka[(t + kLook) % (kLook + 1)] = kread(t + kLook);
-      if (t & 1)
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % (kLook + 1)], qf[t], s1, 0, 0, 0);
-      else
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % (kLook + 1)], qf[t], s0, 0, 0, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-      if (t + kLook < C::NT) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-    }
-
-    // ---- scale (and K=V row factor), mask, exponentiate against m_ref
-    float rk[16];
+  // Logit of key slot r in the log2 domain is s[r] * c[r]: c = the key's
+  // inverse RMS times scale*log2(e) (K=V, from the tile) or scale*log2(e).
+  const float cs = a.scale_log2;
+  auto key_mul = [&](const G4_LDS char* cur, float (&c)[16]) {
     if (TIED) {
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         const f32x4 v = *(const G4_LDS f32x4*)(cur + C::R_OFF + (8 * gq + 4 * hh) * 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rk[4 * gq + i] = v[i];
+        for (int i = 0; i < 4; ++i) c[4 * gq + i] = v[i];
       }
-    }
-    float sv[16];
+    } else {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sv[r] = (s0[r] + s1[r]) * a.scale_log2 * (TIED ? rk[r] : 1.f);
+      for (int r = 0; r < 16; ++r) c[r] = cs;
+    }
+  };
+  // Does tile kt need element masks (some key not visible from some row)?
+  auto edge_tile = [&](int kt) {
     const int key0 = kt * kBN;
-    const bool full = (key0 + kBN - 1 <= tq0) && (a.window == 0 || key0 >= tq1 - a.window + 1);
-    if (!full) {
+    return !((key0 + kBN - 1 <= tq0) && (a.window == 0 || key0 >= tq1 - a.window + 1));
+  };
+  auto visible = [&](int kt, int r) {  // bitwise logic: no short-circuit branches
+    const int d = tq - (kt * kBN + 8 * (r >> 2) + 4 * hh + (r & 3));
+    return (d >= 0) & ((a.window == 0) | (d < a.window));
+  };
+  // Maximum logit of this lane's 16 slots of tile kt (-inf if none visible).
+  auto tile_max = [&](const f32x16& s, const float (&c)[16], int kt) {
+    const bool edge = edge_tile(kt);
+    float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = key0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-        const int d = tq - key;
-        const bool vis = d >= 0 && (a.window == 0 || d < a.window);
-        sv[r] = vis ? sv[r] : -INFINITY;
-      }
+    for (int r = 0; r < 16; ++r) {
+      const float x = s[r] * c[r];
+      mx = fmaxf(mx, ((!edge) | visible(kt, r)) ? x : -INFINITY);
     }
-    float mx = sv[0];
+    return mx;
+  };
+  auto lds_stage = [&](int kt) -> int { return ((kt - kt_lo) & 1) * C::STAGE; };
+
+  // Softmax with a fixed per-row reference m_ref (log2 domain): the row's
+  // maximum over its first tile with a visible key; P = exp2(x - m_ref) is
+  // accumulated without ever rescaling O.  Every P is at most the row sum l,
+  // so a row whose l stays <= 2^64 had no overflow risk; a wave with a larger
+  // (or non-finite) l flags its workgroup, which the REDO launch recomputes
+  // with m_ref = the true row maximum (every P <= 1 then).
+  float m_ref = -INFINITY;
+  if (REDO) {
+    float m_run = -INFINITY;
+    for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+      wait_vmem_all();
+      __syncthreads();
+      const int so = lds_stage(kt);
+      const G4_LDS char* cur = (const G4_LDS char*)smem + so;
+      if (kt < kt_hi) load_tile<D, TIED>(a, lds0 + (C::STAGE - so), kt + 1, b, g, wave, lane);
+      const uint32_t base = lds0 + so;
+      float c[16];
+      key_mul(cur, c);
+      const f32x16 s = qk_tile<D, TIED>(qf, base + koff0, base + koff1, base + kroff0, base + kroff1);
+      m_run = fmaxf(m_run, tile_max(s, c, kt));
+    }
+    m_ref = max_xor32(m_run);
+    __syncthreads();  // every wave is done with the last tile before stage 0 is reloaded
+    load_tile<D, TIED>(a, lds0, kt_lo, b, g, wave, lane);
+  }
+
+  f32x16 oacc[C::NC];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sv[r]);
-    m_true = fmaxf(m_true, mx);
+  for (int c = 0; c < C::NC; ++c) oacc[c] = f32x16{};
+  float l_part = 0.f;
+
+  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+    wait_vmem_all();  // this wave's copies of tile kt have landed
+    __syncthreads();  // all of tile kt is in LDS; every wave is done with tile kt-1
+    const int so = lds_stage(kt);
+    const G4_LDS char* cur = (const G4_LDS char*)smem + so;
+    if (kt < kt_hi) load_tile<D, TIED>(a, lds0 + (C::STAGE - so), kt + 1, b, g, wave, lane);
+
+    // per-key factors first: their LDS reads complete under the K Q^T block
+    const uint32_t base = lds0 + so;
+    float c[16];
+    key_mul(cur, c);
+    const f32x16 s = qk_tile<D, TIED>(qf, base + koff0, base + koff1, base + kroff0, base + kroff1);
+    __builtin_amdgcn_sched_barrier(0);  // keep the factor reads out of the PV read pipeline below
     if (!REDO && __builtin_amdgcn_ballot_w64(m_ref == -INFINITY)) {  // a row meets its first visible key
-      const float rowmx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float rowmx = max_xor32(tile_max(s, c, kt));
       m_ref = m_ref == -INFINITY ? rowmx : m_ref;
     }
     const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = __builtin_fmaf(s[r], c[r], -m_use);
+    if (edge_tile(kt)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = visible(kt, r) ? x[r] : -INFINITY;
+    }
     bf16x8 pb[2];
 #pragma unroll
     for (int mm = 0; mm < 2; ++mm) {
@@ -321,10 +371,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r0 = 8 * mm + 2 * i;
-        float p0 = __builtin_amdgcn_exp2f(sv[r0] - m_use);
-        float p1 = __builtin_amdgcn_exp2f(sv[r0 + 1] - m_use);
+        float p0 = __builtin_amdgcn_exp2f(x[r0]);
+        float p1 = __builtin_amdgcn_exp2f(x[r0 + 1]);
         l_part += p0 + p1;
-        if (TIED) { p0 *= rk[r0]; p1 *= rk[r0 + 1]; }
+        if (TIED) { p0 *= c[r0]; p1 *= c[r0 + 1]; }
         w[i] = pack_bf2(p0, p1);
       }
       pb[mm] = __builtin_bit_cast(bf16x8, w);
@@ -352,17 +402,15 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     }
   }
 
+  // ---- epilogue: flag, normalise, round once to bf16, store
+  const float l_tot = sum_xor32(l_part);
   if (!REDO) {
-    const float mt = fmaxf(m_true, __shfl_xor(m_true, 32, 64));
-    const bool over = mt > m_ref + kHeadroom;
+    const bool over = valid && !(l_tot <= 0x1p64f);
     if (lane == 0) wg_flags[wave] = __builtin_amdgcn_ballot_w64(over) != 0;
-    if (valid && hh == 0) a.mrow[mrow_idx] = mt;
   }
-
-  // ---- epilogue: normalise, round once to bf16, store
-  const float l_tot = l_part + __shfl_xor(l_part, 32, 64);
   if (!valid) return;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  // K=V: P carried the factor c = r * scale*log2(e) / qmul; omul undoes it.
+  const float inv = l_tot > 0.f ? (TIED ? a.omul : 1.f) / l_tot : 0.f;
   uint16_t* orow = a.out + b * a.os[0] + (int64_t)tq * a.os[1] + head * a.os[2];
 #pragma unroll
   for (int c = 0; c < C::NC; ++c) {

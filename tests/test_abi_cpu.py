@@ -71,12 +71,13 @@ def test_prefill_validation():
     assert _prefill(kv, wk=None, v=None) == g4.ERR_NULL
     assert _prefill(kv, wk=FAKE, v=FAKE) == g4.ERR_SHAPE
     assert _prefill(_desc(k_eq_v=True, rotary_dims=512), wk=FAKE, v=None) == g4.ERR_UNSUPPORTED
+    assert _prefill(_desc(k_eq_v=True, scale=2.0 ** 31), wk=FAKE, v=None) == g4.ERR_UNSUPPORTED
     need = g4.g4attn_prefill_workspace_bytes(kv, 1, 16)
-    # row maxima [1, 32, 16] fp32 + flags [1, 4, 1 tile, 4 waves] + r [1, 4, 16] + Krot [1, 4, 16, 128]
-    assert need == 2048 + 256 + 256 + 16 * 4 * 128 * 2
+    # flags [1, 4, 1 tile, 4 waves] + r [1, 4, 16] + Krot [1, 4, 16, 128], each 256-byte aligned
+    assert need == 256 + 256 + 16 * 4 * 128 * 2
     assert _prefill(kv, wk=FAKE, v=None) == g4.ERR_WORKSPACE
     assert _prefill(kv, wk=FAKE, v=None, ws=FAKE, wsb=need - 1) == g4.ERR_WORKSPACE
-    assert g4.g4attn_prefill_workspace_bytes(_desc(), 1, 16) == 2048 + 256
+    assert g4.g4attn_prefill_workspace_bytes(_desc(), 1, 16) == 256
     assert _prefill(_desc()) == g4.ERR_WORKSPACE
 
 
