@@ -28,6 +28,11 @@ CXXFLAGS = [
 ]
 
 
+# Per-source extra flags.  prefill.hip: MFMA builtins write VGPRs (the score
+# tile), because its O accumulator lives in AGPRs via inline assembly.
+EXTRA = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _hipcc():
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if c and os.path.exists(c):
@@ -41,7 +46,7 @@ def sources():
 
 def _compile(src, verbose):
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [_hipcc(), *CXXFLAGS, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *CXXFLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                      if "packed-fp32-ops" not in l)
@@ -52,13 +57,7 @@ def _compile(src, verbose):
     return obj
 
 
-def generate():
-    """Regenerate the assembly include of the prefill kernel (no-op if unchanged)."""
-    subprocess.run([sys.executable, os.path.join(CSRC, "gen_qk_asm.py")], check=True)
-
-
 def build(verbose=False):
-    generate()
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=4) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), sources()))

@@ -182,6 +182,12 @@ g4attn_status g4attn_prefill(const g4attn_layer_desc* d, const g4attn_bf16* q,
   const bool fold = fabsf(c) >= 0x1p-30f;
   a.qmul = fold ? 1.f : c;
   a.omul = fold ? 1.f / c : 1.f;
+  // Per-key factor of the scores: K=V r * (c or 1), r > 0; else c itself,
+  // with the smallest normal float standing in for 0 (the logits are then
+  // below 2^-100 instead of 0, and masked slots still give -inf).
+  if (!d->k_eq_v && c == 0.f) a.scale_log2 = 0x1p-126f;
+  const bool neg = d->k_eq_v ? (fold && c < 0.f) : (a.scale_log2 < 0.f);
+  a.mask_s = neg ? INFINITY : -INFINITY;
   for (int i = 0; i < 3; ++i) { a.qs[i] = q_strides[i]; a.ks[i] = kv_strides[i]; a.os[i] = o_strides[i]; }
   hipStream_t s = (hipStream_t)stream;
   char* wsp = (char*)workspace;

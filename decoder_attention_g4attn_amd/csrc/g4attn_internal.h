@@ -148,8 +148,9 @@ struct PrefillArgs {
   uint16_t* out;
   float* lse;
   int B, S, Hq, Hkv, D, window, kv_tied;
-  float scale_log2;         // scale * log2(e)
+  float scale_log2;         // scale * log2(e), never 0 (FLT_MIN stands in for 0)
   float qmul, omul;         // K=V only: query and output multipliers (see g4attn_prefill)
+  float mask_s;             // score of a masked slot: mask_s * (key factor) = -inf
   int64_t qs[3], ks[3], os[3];
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);

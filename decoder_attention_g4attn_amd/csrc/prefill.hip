@@ -31,7 +31,6 @@
 // distinct bank groups, and the transposing-read addresses stay affine in
 // the dim block.
 #include "g4attn_internal.h"
-#include "prefill_qk_asm.inc"
 
 namespace g4attn {
 namespace {
@@ -49,6 +48,7 @@ struct Cfg {
   static constexpr int R_OFF = KR_OFF + KR_BYTES;
   static constexpr int R_BYTES = TIED ? 256 : 0;
   static constexpr int STAGE = R_OFF + R_BYTES;
+  static constexpr int NST = 3 * STAGE <= 160 * 1024 ? 3 : 2;  // LDS stages
   static constexpr int NT = D / 16;  // QK^T k-steps
   static constexpr int NC = D / 32;  // PV dim blocks
 };
@@ -162,40 +162,45 @@ __device__ __forceinline__ void wg_map(int T, int Hkv, int& b, int& g, int& tile
   tile = T - 1 - r;  // heaviest (latest) rows first
 }
 
-// Scheduling-group masks (LLVM AMDGPU): MFMA, LDS read.
+// Scheduling-group masks (LLVM AMDGPU): VALU (incl. transcendental), MFMA,
+// LDS read.
+constexpr int kSgValu = 0x402;
 constexpr int kSgMfma = 0x008;
 constexpr int kSgDsRead = 0x100;
-constexpr int kLook = 3;  // PV: LDS operand reads issued ahead of their MFMA
+constexpr int kLook = 3;  // LDS operand reads issued ahead of their MFMA
 
-// S^T (32 keys x 32 rows) = K Q^T of one LDS tile, as one assembly block
-// (prefill_qk_asm.inc) that leaves S^T in VGPRs and ends with every LDS read
-// complete and the MFMA result readable.  kb0/kb1 (kr0/kr1): LDS byte
-// addresses of this lane's K (Krot) chunks for even/odd k-steps.
-template <int D, bool TIED>
-__device__ __forceinline__ f32x16 qk_tile(const bf16x8 (&qf)[D / 16], uint32_t kb0, uint32_t kb1,
-                                          uint32_t kr0, uint32_t kr1) {
-  f32x16 s;
-  bf16x8 tmp[G4_QK_TEMPS];
-  if constexpr (TIED) {
-    asm volatile(G4_QK_ASM_512_TIED
-                 : G4_QK_OUTS
-                 : G4_QK_Q32, [kb0] "v"(kb0), [kb1] "v"(kb1), [kr0] "v"(kr0), [kr1] "v"(kr1)
-                 : "memory");
-  } else if constexpr (D == 512) {
-    asm volatile(G4_QK_ASM_512 : G4_QK_OUTS : G4_QK_Q32, [kb0] "v"(kb0), [kb1] "v"(kb1) : "memory");
-  } else {
-    asm volatile(G4_QK_ASM_256 : G4_QK_OUTS : G4_QK_Q16, [kb0] "v"(kb0), [kb1] "v"(kb1) : "memory");
-  }
-  return s;
+// O^T block += V^T P^T on the AGPR accumulator.  Written as assembly so that
+// the compiler never allocates O (all AGPRs at D = 512) on the VGPR side;
+// being volatile, these also keep the LDS reads around them in source order.
+// `FIRST`: the first use of a P^T operand written by VALU just before (an
+// MFMA needs 2 wait states after a VALU write of its source).
+template <bool FIRST>
+__device__ __forceinline__ void mfma_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  if (FIRST)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
+
+// Keeps a value computed before this point (no code is emitted).
+__device__ __forceinline__ void pin(float& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void pin(uint32_t& v) { asm volatile("" : "+v"(v)); }
 
 // REDO = false: main pass.  REDO = true: recompute the workgroups whose main
 // pass flagged a reference overflow, after a first sweep that finds each
 // row's true maximum.
+//
+// Software pipeline (per wave, one wave per SIMD): iteration kt computes
+// S(kt+1) = K(kt+1) Q^T with its MFMAs interleaved with the softmax VALU
+// work of S(kt), then O += V(kt)^T P(kt)^T.  Tiles kt and kt+1 are resident
+// in LDS while tile kt+2 is in flight (NST = 3 stages); configurations
+// whose three stages do not fit (D = 512 without K=V) use two stages and
+// load tile kt+2 after PV(kt).
 template <int D, bool TIED, bool REDO>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   typedef Cfg<D, TIED> C;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE];
+  constexpr int NST = C::NST;
+  __shared__ __attribute__((aligned(1024))) char smem[NST * C::STAGE];
   const uint32_t lds0 = lds_addr((G4_LDS void*)smem);  // LDS byte address of stage 0
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -221,10 +226,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     if ((wg_flags[0] | wg_flags[1] | wg_flags[2] | wg_flags[3]) == 0) return;
   }
 
-  // Prefetch the first tile, then load this lane's Q^T fragments (rows past S
-  // read row S-1; their results are never stored).  K=V: the K-norm weight
-  // is folded into the non-rotated dims, times qmul.
+  // Prefetch the first two tiles, then load this lane's Q^T fragments (rows
+  // past S read row S-1; their results are never stored).  K=V: the K-norm
+  // weight is folded into the non-rotated dims, times qmul.
   load_tile<D, TIED>(a, lds0, kt_lo, b, g, wave, lane);
+  if (kt_lo < kt_hi) load_tile<D, TIED>(a, lds0 + C::STAGE, kt_lo + 1, b, g, wave, lane);
 
   bf16x8 qf[C::NT];
   {
@@ -270,14 +276,25 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       toff[m][u] = vbase + kv_row_off<D>(R) + (tqd & 1) * 8 + 16 * (tr_chunk ^ kv_xor<D>(R));
     }
 
+  auto lds_ptr = [&](int so) { return (const G4_LDS char*)smem + so; };
+  // K fragment of k-step t of the tile in stage `so` (K=V: rotated k-steps
+  // read the Krot slice, chunk 2u + hh with u = t (t < 4) or t - 12).
+  auto kread = [&](int so, int t) -> bf16x8 {
+    if (TIED && rot_step(t)) {
+      const int u = t < 4 ? t : t - 12;
+      return lds_read_b128(lds_ptr(so) + ((u & 1) ? kroff1 : kroff0) + 64 * (u >> 1));
+    }
+    return lds_read_b128(lds_ptr(so) + ((t & 1) ? koff1 : koff0) + 64 * (t >> 1));
+  };
+
   // Logit of key slot r in the log2 domain is s[r] * c[r]: c = the key's
   // inverse RMS times scale*log2(e) (K=V, from the tile) or scale*log2(e).
   const float cs = a.scale_log2;
-  auto key_mul = [&](const G4_LDS char* cur, float (&c)[16]) {
+  auto key_mul = [&](int so, float (&c)[16]) {
     if (TIED) {
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        const f32x4 v = *(const G4_LDS f32x4*)(cur + C::R_OFF + (8 * gq + 4 * hh) * 4);
+        const f32x4 v = *(const G4_LDS f32x4*)(lds_ptr(so) + C::R_OFF + (8 * gq + 4 * hh) * 4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) c[4 * gq + i] = v[i];
       }
@@ -306,7 +323,20 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     }
     return mx;
   };
-  auto lds_stage = [&](int kt) -> int { return ((kt - kt_lo) & 1) * C::STAGE; };
+
+  // S^T(tile in stage so) = K Q^T, K reads kLook ahead of their MFMA.
+  auto qk = [&](int so) -> f32x16 {
+    bf16x8 ka[kLook + 1];
+#pragma unroll
+    for (int t = 0; t < kLook; ++t) ka[t] = kread(so, t);
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t) {
+      if (t + kLook < C::NT) ka[(t + kLook) % (kLook + 1)] = kread(so, t + kLook);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % (kLook + 1)], qf[t], s, 0, 0, 0);
+    }
+    return s;
+  };
 
   // Softmax with a fixed per-row reference m_ref (log2 domain): the row's
   // maximum over its first tile with a visible key; P = exp2(x - m_ref) is
@@ -315,92 +345,190 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   // (or non-finite) l flags its workgroup, which the REDO launch recomputes
   // with m_ref = the true row maximum (every P <= 1 then).
   float m_ref = -INFINITY;
-  if (REDO) {
-    float m_run = -INFINITY;
-    for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-      wait_vmem_all();
-      __syncthreads();
-      const int so = lds_stage(kt);
-      const G4_LDS char* cur = (const G4_LDS char*)smem + so;
-      if (kt < kt_hi) load_tile<D, TIED>(a, lds0 + (C::STAGE - so), kt + 1, b, g, wave, lane);
-      const uint32_t base = lds0 + so;
-      float c[16];
-      key_mul(cur, c);
-      const f32x16 s = qk_tile<D, TIED>(qf, base + koff0, base + koff1, base + kroff0, base + kroff1);
-      m_run = fmaxf(m_run, tile_max(s, c, kt));
-    }
-    m_ref = max_xor32(m_run);
-    __syncthreads();  // every wave is done with the last tile before stage 0 is reloaded
-    load_tile<D, TIED>(a, lds0, kt_lo, b, g, wave, lane);
-  }
-
-  f32x16 oacc[C::NC];
-#pragma unroll
-  for (int c = 0; c < C::NC; ++c) oacc[c] = f32x16{};
   float l_part = 0.f;
-
-  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-    wait_vmem_all();  // this wave's copies of tile kt have landed
-    __syncthreads();  // all of tile kt is in LDS; every wave is done with tile kt-1
-    const int so = lds_stage(kt);
-    const G4_LDS char* cur = (const G4_LDS char*)smem + so;
-    if (kt < kt_hi) load_tile<D, TIED>(a, lds0 + (C::STAGE - so), kt + 1, b, g, wave, lane);
-
-    // per-key factors first: their LDS reads complete under the K Q^T block
-    const uint32_t base = lds0 + so;
-    float c[16];
-    key_mul(cur, c);
-    const f32x16 s = qk_tile<D, TIED>(qf, base + koff0, base + koff1, base + kroff0, base + kroff1);
-    __builtin_amdgcn_sched_barrier(0);  // keep the factor reads out of the PV read pipeline below
+  // Masked slots of an edge tile: s = mask_s makes s * c = -inf.
+  auto mask_edge = [&](f32x16& s, int kt) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = visible(kt, r) ? s[r] : a.mask_s;
+  };
+  auto first_visible = [&](const f32x16& s, const float (&c)[16], int kt) {
     if (!REDO && __builtin_amdgcn_ballot_w64(m_ref == -INFINITY)) {  // a row meets its first visible key
       const float rowmx = max_xor32(tile_max(s, c, kt));
       m_ref = m_ref == -INFINITY ? rowmx : m_ref;
     }
-    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-    float x[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = __builtin_fmaf(s[r], c[r], -m_use);
-    if (edge_tile(kt)) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = visible(kt, r) ? x[r] : -INFINITY;
+  };
+  // The softmax of one score tile as a list of micro-ops, stage by stage so
+  // that no op waits on the one before it: 16 FMA (x = s c - m), 16 EXP2,
+  // 8 pair sums, 8 row-sum adds, (K=V) 16 multiplies by c, 8 bf16 packs.
+  constexpr int kSmOps = TIED ? 72 : 56;
+  struct Sm {
+    float x[16], ps[8];
+    uint32_t w[8];
+  };
+  // Each op's result is pinned (an empty asm that takes it in and out), so
+  // the op stays in its slot instead of sinking towards the result's use.
+  auto sm_op = [&](Sm& st, const f32x16& s, const float (&c)[16], float m_use, int j) {
+    if (j < 16) {
+      st.x[j] = __builtin_fmaf(s[j], c[j], -m_use);
+      pin(st.x[j]);
+    } else if (j < 32) {
+      st.x[j - 16] = __builtin_amdgcn_exp2f(st.x[j - 16]);
+      pin(st.x[j - 16]);
+    } else if (j < 40) {
+      st.ps[j - 32] = st.x[2 * (j - 32)] + st.x[2 * (j - 32) + 1];
+      pin(st.ps[j - 32]);
+    } else if (j < 48) {
+      l_part += st.ps[j - 40];
+      pin(l_part);
+    } else if (TIED && j < 64) {
+      st.x[j - 48] *= c[j - 48];
+      pin(st.x[j - 48]);
+    } else {
+      const int i = j - (TIED ? 64 : 48);
+      st.w[i] = pack_bf2(st.x[2 * i], st.x[2 * i + 1]);
+      pin(st.w[i]);
     }
-    bf16x8 pb[2];
+  };
+  auto sm_out = [&](const Sm& st, bf16x8 (&pb)[2]) {
 #pragma unroll
     for (int mm = 0; mm < 2; ++mm) {
-      u32x4 w;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r0 = 8 * mm + 2 * i;
-        float p0 = __builtin_amdgcn_exp2f(x[r0]);
-        float p1 = __builtin_amdgcn_exp2f(x[r0 + 1]);
-        l_part += p0 + p1;
-        if (TIED) { p0 *= c[r0]; p1 *= c[r0 + 1]; }
-        w[i] = pack_bf2(p0, p1);
-      }
+      const u32x4 w = {st.w[4 * mm], st.w[4 * mm + 1], st.w[4 * mm + 2], st.w[4 * mm + 3]};
       pb[mm] = __builtin_bit_cast(bf16x8, w);
     }
+  };
+  // P^T operands of score tile s (K=V: P times the key factor).
+  auto softmax = [&](const f32x16& s, const float (&c)[16], bf16x8 (&pb)[2]) {
+    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+    Sm st;
+#pragma unroll
+    for (int j = 0; j < kSmOps; ++j) sm_op(st, s, c, m_use, j);
+    sm_out(st, pb);
+  };
+  // S^T of the tile in stage so, with the softmax of s_prev spread over its
+  // MFMAs: each MFMA is followed by its share of the micro-ops, fenced so the
+  // scheduler keeps this order (the ops run while the MFMA does).
+  auto qk_softmax = [&](int so, const f32x16& s_prev, const float (&c)[16], bf16x8 (&pb)[2]) -> f32x16 {
+    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+    Sm st;
+    bf16x8 ka[kLook + 1];
+#pragma unroll
+    for (int t = 0; t < kLook; ++t) ka[t] = kread(so, t);
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t) {
+      if (t + kLook < C::NT) ka[(t + kLook) % (kLook + 1)] = kread(so, t + kLook);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % (kLook + 1)], qf[t], s, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = kSmOps * t / C::NT; j < kSmOps * (t + 1) / C::NT; ++j) sm_op(st, s_prev, c, m_use, j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    sm_out(st, pb);
+    return s;
+  };
 
-    // ---- O^T += V^T P^T, transposing reads kLook MFMAs ahead
+  f32x16 oacc[C::NC];
+#pragma unroll
+  for (int c = 0; c < C::NC; ++c) oacc[c] = f32x16{};
+  // O^T += V^T P^T over the tile in stage so, transposing reads kLook ahead.
+  auto pv = [&](int so, const bf16x8 (&pb)[2]) {
     constexpr int NPV = 2 * C::NC;  // (mm, c) pairs
     auto vread = [&](int i) -> bf16x8 {
       const int mm = i / C::NC, c = i % C::NC;
-      const i16x4 lo = lds_read_tr16(cur + toff[mm][0] + 64 * c);
-      const i16x4 hi = lds_read_tr16(cur + toff[mm][1] + 64 * c);
+      const i16x4 lo = lds_read_tr16(lds_ptr(so) + toff[mm][0] + 64 * c);
+      const i16x4 hi = lds_read_tr16(lds_ptr(so) + toff[mm][1] + 64 * c);
       return cat_tr(lo, hi);
     };
     bf16x8 va[kLook + 1];
 #pragma unroll
     for (int i = 0; i < kLook; ++i) va[i] = vread(i);
-    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2 * kLook, 0);
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
       if (i + kLook < NPV) va[(i + kLook) % (kLook + 1)] = vread(i + kLook);
       const int mm = i / C::NC, c = i % C::NC;
-      oacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % (kLook + 1)], pb[mm], oacc[c], 0, 0, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-      if (i + kLook < NPV) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+      if (c == 0)
+        mfma_acc<true>(oacc[c], va[i % (kLook + 1)], pb[mm]);
+      else
+        mfma_acc<false>(oacc[c], va[i % (kLook + 1)], pb[mm]);
     }
+  };
+
+  if (REDO) {
+    // first sweep: the true maximum of every row (stages 0 and 1 hold kt_lo
+    // and kt_lo + 1 already; two-stage ring)
+    float m_run = -INFINITY;
+    int so = 0;
+    for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+      wait_vmem_all();
+      __syncthreads();  // tile kt (and kt + 1) landed; every wave is done with tile kt - 1
+      if (kt > kt_lo && kt < kt_hi) load_tile<D, TIED>(a, lds0 + (C::STAGE - so), kt + 1, b, g, wave, lane);
+      float c[16];
+      key_mul(so, c);
+      const f32x16 s = qk(so);
+      m_run = fmaxf(m_run, tile_max(s, c, kt));
+      so = C::STAGE - so;
+    }
+    m_ref = max_xor32(m_run);
+    __syncthreads();  // every wave is done before the stages are reloaded
+    load_tile<D, TIED>(a, lds0, kt_lo, b, g, wave, lane);
+    if (kt_lo < kt_hi) load_tile<D, TIED>(a, lds0 + C::STAGE, kt_lo + 1, b, g, wave, lane);
   }
+
+  wait_vmem_all();
+  __syncthreads();
+  // One pipeline step: softmax + PV of tile kt (scores s_cur) and the scores
+  // of tile kt + 1 into s_nxt.  Written out twice per loop trip with the two
+  // score registers swapped, so neither is ever copied.
+  int so_cur = 0, so_nxt = C::STAGE, so_ld = NST == 3 ? 2 * C::STAGE : 0;
+  auto step = [&](int kt, f32x16& s_cur, f32x16& s_nxt) {
+    wait_vmem_all();  // this wave's copies of tile kt+1 have landed
+    __syncthreads();  // all of tile kt+1 is in LDS; every wave is done with tile kt-1
+    if (NST == 3 && kt + 2 <= kt_hi) load_tile<D, TIED>(a, lds0 + so_ld, kt + 2, b, g, wave, lane);
+    float c[16];
+    key_mul(so_cur, c);
+    first_visible(s_cur, c, kt);
+    if (edge_tile(kt)) mask_edge(s_cur, kt);
+    bf16x8 pb[2];
+    s_nxt = qk_softmax(so_nxt, s_cur, c, pb);
+    __builtin_amdgcn_sched_barrier(0);
+    pv(so_cur, pb);
+    if (NST == 2 && kt + 2 <= kt_hi) {
+      __syncthreads();  // every wave is done with tile kt
+      load_tile<D, TIED>(a, lds0 + so_cur, kt + 2, b, g, wave, lane);
+    }
+    const int t = so_cur;
+    so_cur = so_nxt;
+    if (NST == 3) { so_nxt = so_ld; so_ld = t; } else { so_nxt = t; }
+  };
+  auto last = [&](f32x16& s_cur) {
+    float c[16];
+    key_mul(so_cur, c);
+    first_visible(s_cur, c, kt_hi);
+    if (edge_tile(kt_hi)) mask_edge(s_cur, kt_hi);
+    bf16x8 pb[2];
+    softmax(s_cur, c, pb);
+    pv(so_cur, pb);
+  };
+  f32x16 sa = qk(0), sb;
+  int kt = kt_lo;
+  for (; kt + 1 < kt_hi; kt += 2) {
+    step(kt, sa, sb);
+    step(kt + 1, sb, sa);
+  }
+  if (kt < kt_hi) {
+    step(kt, sa, sb);
+    sa = sb;
+  }
+  last(sa);
+  // the last MFMA results are read below: 18 wait states cover an 8-pass XDL
+  asm volatile("s_nop 15\n\ts_nop 1"
+               : "+a"(oacc[0]), "+a"(oacc[1]), "+a"(oacc[2]), "+a"(oacc[3]), "+a"(oacc[4]), "+a"(oacc[5]),
+                 "+a"(oacc[6]), "+a"(oacc[7]));
+  if constexpr (C::NC > 8)
+    asm volatile(""
+                 : "+a"(oacc[8 % C::NC]), "+a"(oacc[9 % C::NC]), "+a"(oacc[10 % C::NC]),
+                   "+a"(oacc[11 % C::NC]), "+a"(oacc[12 % C::NC]), "+a"(oacc[13 % C::NC]),
+                   "+a"(oacc[14 % C::NC]), "+a"(oacc[15 % C::NC]));
 
   // ---- epilogue: flag, normalise, round once to bf16, store
   const float l_tot = sum_xor32(l_part);
