@@ -168,6 +168,8 @@ g4attn_status g4attn_prefill(const g4attn_layer_desc* d, const g4attn_bf16* q,
       !aligned16(out) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
     return G4ATTN_ERR_LAYOUT;
   if (!strides_ok(q_strides) || !strides_ok(kv_strides) || !strides_ok(o_strides)) return G4ATTN_ERR_LAYOUT;
+  // a K/V tile's 32 row offsets are formed in 32 bits
+  if (kv_strides[1] >= ((int64_t)1 << 25)) return G4ATTN_ERR_UNSUPPORTED;
   const PrefillWs ws = prefill_ws(d, B, S);
   if (!workspace || workspace_bytes < ws.total || !aligned16(workspace)) return G4ATTN_ERR_WORKSPACE;
 

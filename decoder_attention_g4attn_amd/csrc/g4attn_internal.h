@@ -85,6 +85,15 @@ __device__ __forceinline__ void g2lds4s(const void* sbase, uint32_t voff, uint32
                : "memory", "m0");
 }
 
+// As g2lds16s with the LDS destination formed in m0 as `lds + imm`
+// (`lds` wave-uniform, `imm` a compile-time byte offset).
+template <int IMM>
+__device__ __forceinline__ void g2lds16si(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(__builtin_amdgcn_readfirstlane(lds)), "i"(IMM)
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ bf16x8 lds_read_b128(const G4_LDS char* p) {
   return *(const G4_LDS bf16x8*)p;
 }

@@ -30,6 +30,8 @@
 // 4-row x 64-byte pattern of the transposing read (PV operand) both hit
 // distinct bank groups, and the transposing-read addresses stay affine in
 // the dim block.
+#include <type_traits>
+
 #include "g4attn_internal.h"
 
 namespace g4attn {
@@ -67,57 +69,81 @@ __device__ __forceinline__ int kr_xor(int R) { return (R >> 2) & 3; }
 // Is the 16-dim k-step t one of the rotated (Krot) dims 0..63 / 256..319?
 __device__ __forceinline__ constexpr bool rot_step(int t) { return t < 4 || (t >= 16 && t < 20); }
 
-// Global->LDS copy of key tile kt.  The tile's base address is wave-uniform
-// (scalar registers) and each lane adds an unsigned 32-bit byte offset (the
-// scalar-base form of the load).  FULL: all 32 keys are < S; otherwise rows
-// past S re-read row S-1 (they are masked).
-template <int D, bool TIED, bool FULL>
-__device__ __forceinline__ void load_tile_rows(const PrefillArgs& a, uint32_t stage, int kt, int b, int g,
-                                               int wave, int lane) {
-  typedef Cfg<D, TIED> C;
+// Global->LDS copy of key tile kt, one load instruction ("piece") at a time
+// so that the copies can be spread over the MFMAs of a tile step instead of
+// stalling every wave in one burst.  The tile's row bases are wave-uniform
+// (scalar registers) plus an unsigned 32-bit per-lane byte offset (the
+// scalar-base form).  Rows past S re-read row S-1 (they are masked).
+// Pieces per wave: D = 512: 8 rows of K (or X), then 8 of V; D = 256: 4
+// instructions of two rows for K, then 4 for V; K=V: then 2 of the Krot
+// slice and (wave 0) the 32 key factors.
+template <int D, bool TIED>
+struct TilePieces {
+  static constexpr int KV = (D == 512 ? 8 : 4) * (TIED ? 1 : 2);
+  static constexpr int N = KV + (TIED ? 3 : 0);
+};
+
+// Per-tile source addresses of the copy (wave-uniform, formed once per tile).
+struct TileSrc {
+  const char* k;      // K (or X) row key0 of this (b, g)
+  const char* v;      // V row key0
+  const char* krot;   // K=V: Krot row key0
+  const float* r;     // K=V: key factors from key0
+  uint32_t last_off;  // byte offset of the last in-range row (S-1) from row key0
+  int last;           // its index
+};
+
+template <int D, bool TIED>
+__device__ __forceinline__ TileSrc tile_src(const PrefillArgs& a, int kt, int b, int g) {
   const int key0 = kt * kBN;
-  const int last = a.S - 1 - key0;  // last in-range row of the tile
-  const int64_t rs = a.ks[1] * 2;   // key stride in bytes
-  auto row_off = [&](int R) -> int64_t { return (int64_t)(FULL ? R : min(R, last)) * rs; };
-  const int64_t tb = (b * a.ks[0] + g * a.ks[2] + (int64_t)key0 * a.ks[1]) * 2;
-  const int ntile = TIED ? 1 : 2;
-#pragma unroll
-  for (int which = 0; which < ntile; ++which) {
-    const char* src = (const char*)(which == 0 ? a.k : a.v) + tb;
+  TileSrc t;
+  const int64_t e = b * a.ks[0] + g * a.ks[2] + (int64_t)key0 * a.ks[1];
+  t.k = (const char*)(a.k + e);
+  t.v = TIED ? nullptr : (const char*)(a.v + e);
+  const int64_t row0 = ((int64_t)b * a.Hkv + g) * a.S + key0;
+  t.krot = TIED ? (const char*)(a.krot + row0 * 128) : nullptr;
+  t.r = TIED ? a.r + row0 : nullptr;
+  t.last = a.S - 1 - key0;
+  t.last_off = (uint32_t)t.last * (uint32_t)(a.ks[1] * 2);
+  return t;
+}
+
+// Row offsets grow with the row, so clamping a row to S-1 is a min() of
+// byte offsets; the lane's own 16-byte chunk rides in the same 32-bit
+// offset (the key stride times 32 fits in 31 bits, checked on the host).
+template <int D, bool TIED>
+__device__ __forceinline__ void load_piece(const PrefillArgs& a, const TileSrc& ts, uint32_t stage, int wave,
+                                           int lane, int piece) {
+  typedef Cfg<D, TIED> C;
+  constexpr int PER = D == 512 ? 8 : 4;  // pieces per K or V tile
+  const uint32_t rs = (uint32_t)(a.ks[1] * 2);  // key stride in bytes
+  if (piece < TilePieces<D, TIED>::KV) {
+    const int which = piece / PER, i = piece % PER;
+    const char* src = which == 0 ? ts.k : ts.v;
     const uint32_t tile = stage + which * C::KT_BYTES;
     if (D == 512) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int R = wave * 8 + i;
-        const uint32_t off = (uint32_t)(lane ^ kv_xor<D>(R)) * 16u;
-        g2lds16s(src + row_off(R), off, tile + kv_row_off<D>(R));
-      }
+      const int R = wave * 8 + i;
+      const uint32_t row = min((uint32_t)R * rs, ts.last_off);
+      const uint32_t off = row + (uint32_t)(lane ^ kv_xor<D>(R)) * 16u;
+      g2lds16s(src, off, tile + kv_row_off<D>(R));
     } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // lanes 0..31 copy row s, lanes 32..63 row s + 16
-        const int s = wave * 4 + i;
-        const uint32_t d = (uint32_t)(row_off(s + 16) - row_off(s));
-        const uint32_t off = (lane >> 5) * d + (uint32_t)((lane & 31) ^ kv_xor<D>(s)) * 16u;
-        g2lds16s(src + row_off(s), off, tile + s * kSeg);
-      }
+      // lanes 0..31 copy row s, lanes 32..63 row s + 16
+      const int s = wave * 4 + i;
+      const uint32_t r0 = min((uint32_t)s * rs, ts.last_off);
+      const uint32_t r1 = min((uint32_t)(s + 16) * rs, ts.last_off);
+      const uint32_t off = ((lane >> 5) ? r1 : r0) + (uint32_t)((lane & 31) ^ kv_xor<D>(s)) * 16u;
+      g2lds16s(src, off, tile + s * kSeg);
     }
-  }
-  if (TIED) {
-    const int64_t row0 = ((int64_t)b * a.Hkv + g) * a.S + key0;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
+  } else if (TIED) {
+    const int i = piece - TilePieces<D, TIED>::KV;
+    if (i < 2) {
       const int s = wave * 2 + i;
       // lanes 16q .. 16q+15 copy Krot row s + 8q
       const int R = s + 8 * (lane >> 4);
-      const int Re = FULL ? R : min(R, last);
-      const uint32_t off = (uint32_t)Re * 256u + (uint32_t)((lane & 15) ^ kr_xor(R)) * 16u;
-      g2lds16s(a.krot + row0 * 128, off, stage + C::KR_OFF + s * kSeg);
-    }
-    if (wave == 0) {
-      const int R = lane & 31;
-      const int Re = FULL ? R : min(R, last);
-      g2lds4s(a.r + row0, (uint32_t)Re * 4u, stage + C::R_OFF);
+      const uint32_t off = (uint32_t)min(R, ts.last) * 256u + (uint32_t)((lane & 15) ^ kr_xor(R)) * 16u;
+      g2lds16s(ts.krot, off, stage + C::KR_OFF + s * kSeg);
+    } else if (wave == 0) {
+      g2lds4s(ts.r, (uint32_t)min(lane & 31, ts.last) * 4u, stage + C::R_OFF);
     }
   }
 }
@@ -125,10 +151,9 @@ __device__ __forceinline__ void load_tile_rows(const PrefillArgs& a, uint32_t st
 template <int D, bool TIED>
 __device__ __forceinline__ void load_tile(const PrefillArgs& a, uint32_t stage, int kt, int b, int g,
                                           int wave, int lane) {
-  if (kt * kBN + kBN <= a.S)
-    load_tile_rows<D, TIED, true>(a, stage, kt, b, g, wave, lane);
-  else
-    load_tile_rows<D, TIED, false>(a, stage, kt, b, g, wave, lane);
+  const TileSrc ts = tile_src<D, TIED>(a, kt, b, g);
+#pragma unroll
+  for (int p = 0; p < TilePieces<D, TIED>::N; ++p) load_piece<D, TIED>(a, ts, stage, wave, lane, p);
 }
 
 // Workgroup -> (batch b, KV group g, row tile) for the 8 XCDs of the chip.
@@ -407,7 +432,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   // S^T of the tile in stage so, with the softmax of s_prev spread over its
   // MFMAs: each MFMA is followed by its share of the micro-ops, fenced so the
   // scheduler keeps this order (the ops run while the MFMA does).
-  auto qk_softmax = [&](int so, const f32x16& s_prev, const float (&c)[16], bf16x8 (&pb)[2]) -> f32x16 {
+  // With LOADS, the copy of tile ld_kt into stage ld_so rides along, one
+  // piece after every other MFMA.
+  auto qk_softmax = [&](int so, const f32x16& s_prev, const float (&c)[16], bf16x8 (&pb)[2], auto loads,
+                        int ld_so, int ld_kt) -> f32x16 {
+    constexpr bool LOADS = decltype(loads)::value;
+    const TileSrc ts = tile_src<D, TIED>(a, ld_kt, b, g);
     const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
     Sm st;
     bf16x8 ka[kLook + 1];
@@ -421,6 +451,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = kSmOps * t / C::NT; j < kSmOps * (t + 1) / C::NT; ++j) sm_op(st, s_prev, c, m_use, j);
+      if (LOADS && (t & 1) == 0 && (t >> 1) < TilePieces<D, TIED>::N)
+        load_piece<D, TIED>(a, ts, lds0 + ld_so, wave, lane, t >> 1);
       __builtin_amdgcn_sched_barrier(0);
     }
     sm_out(st, pb);
@@ -483,13 +515,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   auto step = [&](int kt, f32x16& s_cur, f32x16& s_nxt) {
     wait_vmem_all();  // this wave's copies of tile kt+1 have landed
     __syncthreads();  // all of tile kt+1 is in LDS; every wave is done with tile kt-1
-    if (NST == 3 && kt + 2 <= kt_hi) load_tile<D, TIED>(a, lds0 + so_ld, kt + 2, b, g, wave, lane);
     float c[16];
     key_mul(so_cur, c);
     first_visible(s_cur, c, kt);
     if (edge_tile(kt)) mask_edge(s_cur, kt);
     bf16x8 pb[2];
-    s_nxt = qk_softmax(so_nxt, s_cur, c, pb);
+    // three stages: tile kt+2 goes to the stage tile kt-1 left (past the
+    // end, the last tile is copied again into that unused stage)
+    s_nxt = qk_softmax(so_nxt, s_cur, c, pb, std::integral_constant<bool, NST == 3>{}, so_ld, min(kt + 2, kt_hi));
     __builtin_amdgcn_sched_barrier(0);
     pv(so_cur, pb);
     if (NST == 2 && kt + 2 <= kt_hi) {
@@ -520,6 +553,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     sa = sb;
   }
   last(sa);
+  wait_vmem_all();  // the extra copy of the last tile has landed before the wave ends
   // the last MFMA results are read below: 18 wait states cover an 8-pass XDL
   asm volatile("s_nop 15\n\ts_nop 1"
                : "+a"(oacc[0]), "+a"(oacc[1]), "+a"(oacc[2]), "+a"(oacc[3]), "+a"(oacc[4]), "+a"(oacc[5]),
