@@ -333,9 +333,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     const int key0 = kt * kBN;
     return !((key0 + kBN - 1 <= tq0) && (a.window == 0 || key0 >= tq1 - a.window + 1));
   };
-  auto visible = [&](int kt, int r) {  // bitwise logic: no short-circuit branches
-    const int d = tq - (kt * kBN + 8 * (r >> 2) + 4 * hh + (r & 3));
-    return (d >= 0) & ((a.window == 0) | (d < a.window));
+  // Key slot r of tile kt is visible iff 0 <= d < w_eff with d = tq - key:
+  // one unsigned compare (a global layer takes w_eff = 2^31 - 1).
+  const uint32_t w_eff = a.window ? (uint32_t)a.window : 0x7fffffffu;
+  auto visible = [&](int kt, int r) {
+    const uint32_t d = (uint32_t)(tq - 4 * hh - kt * kBN) - (uint32_t)(8 * (r >> 2) + (r & 3));
+    return d < w_eff;
   };
   // Maximum logit of this lane's 16 slots of tile kt (-inf if none visible).
   auto tile_max = [&](const f32x16& s, const float (&c)[16], int kt) {
@@ -370,7 +373,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   // (or non-finite) l flags its workgroup, which the REDO launch recomputes
   // with m_ref = the true row maximum (every P <= 1 then).
   float m_ref = -INFINITY;
-  float l_part = 0.f;
+  float l_part[4] = {0.f, 0.f, 0.f, 0.f};  // four partial row sums: no serial add chain
   // Masked slots of an edge tile: s = mask_s makes s * c = -inf.
   auto mask_edge = [&](f32x16& s, int kt) {
 #pragma unroll
@@ -403,8 +406,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       st.ps[j - 32] = st.x[2 * (j - 32)] + st.x[2 * (j - 32) + 1];
       pin(st.ps[j - 32]);
     } else if (j < 48) {
-      l_part += st.ps[j - 40];
-      pin(l_part);
+      l_part[(j - 40) & 3] += st.ps[j - 40];
+      pin(l_part[(j - 40) & 3]);
     } else if (TIED && j < 64) {
       st.x[j - 48] *= c[j - 48];
       pin(st.x[j - 48]);
@@ -434,15 +437,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   // scheduler keeps this order (the ops run while the MFMA does).
   // With LOADS, the copy of tile ld_kt into stage ld_so rides along, one
   // piece after every other MFMA.
-  auto qk_softmax = [&](int so, const f32x16& s_prev, const float (&c)[16], bf16x8 (&pb)[2], auto loads,
-                        int ld_so, int ld_kt) -> f32x16 {
+  // ka[0 .. kLook-1] hold the first K fragments, read by the caller.
+  auto qk_softmax = [&](int so, bf16x8 (&ka)[kLook + 1], const f32x16& s_prev, const float (&c)[16],
+                        bf16x8 (&pb)[2], auto loads, int ld_so, int ld_kt) -> f32x16 {
     constexpr bool LOADS = decltype(loads)::value;
     const TileSrc ts = tile_src<D, TIED>(a, ld_kt, b, g);
     const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
     Sm st;
-    bf16x8 ka[kLook + 1];
-#pragma unroll
-    for (int t = 0; t < kLook; ++t) ka[t] = kread(so, t);
     f32x16 s = f32x16{};
 #pragma unroll
     for (int t = 0; t < C::NT; ++t) {
@@ -515,6 +516,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   auto step = [&](int kt, f32x16& s_cur, f32x16& s_nxt) {
     wait_vmem_all();  // this wave's copies of tile kt+1 have landed
     __syncthreads();  // all of tile kt+1 is in LDS; every wave is done with tile kt-1
+    // first K fragments of tile kt+1 right away: their latency hides under
+    // the bookkeeping below
+    bf16x8 ka[kLook + 1];
+#pragma unroll
+    for (int t = 0; t < kLook; ++t) ka[t] = kread(so_nxt, t);
     float c[16];
     key_mul(so_cur, c);
     first_visible(s_cur, c, kt);
@@ -522,7 +528,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     bf16x8 pb[2];
     // three stages: tile kt+2 goes to the stage tile kt-1 left (past the
     // end, the last tile is copied again into that unused stage)
-    s_nxt = qk_softmax(so_nxt, s_cur, c, pb, std::integral_constant<bool, NST == 3>{}, so_ld, min(kt + 2, kt_hi));
+    s_nxt = qk_softmax(so_nxt, ka, s_cur, c, pb, std::integral_constant<bool, NST == 3>{}, so_ld, min(kt + 2, kt_hi));
     __builtin_amdgcn_sched_barrier(0);
     pv(so_cur, pb);
     if (NST == 2 && kt + 2 <= kt_hi) {
@@ -565,7 +571,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
                    "+a"(oacc[14 % C::NC]), "+a"(oacc[15 % C::NC]));
 
   // ---- epilogue: flag, normalise, round once to bf16, store
-  const float l_tot = sum_xor32(l_part);
+  const float l_tot = sum_xor32((l_part[0] + l_part[1]) + (l_part[2] + l_part[3]));
   if (!REDO) {
     const bool over = valid && !(l_tot <= 0x1p64f);
     if (lane == 0) wg_flags[wave] = __builtin_amdgcn_ballot_w64(over) != 0;

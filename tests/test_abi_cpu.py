@@ -66,6 +66,8 @@ def test_prefill_validation():
     assert _prefill(_desc(), B=0) == g4.ERR_SHAPE
     assert _prefill(_desc(), q=MISALIGNED) == g4.ERR_LAYOUT
     assert _prefill(_desc(), qs=I64(16 * 32 * 512, 32 * 512, 511)) == g4.ERR_LAYOUT
+    # K/V row strides of 2^25 elements or more: tile row offsets would overflow 32 bits
+    assert _prefill(_desc(), ks=I64(16 * (1 << 25), 1 << 25, 512), ws=FAKE, wsb=1 << 30) == g4.ERR_UNSUPPORTED
     # K=V layer: one tensor, K weight required, D = 512 with 128 rotated dims
     kv = _desc(k_eq_v=True)
     assert _prefill(kv, wk=None, v=None) == g4.ERR_NULL
