@@ -66,36 +66,30 @@ class Stage:
         self.ms = []
 
 
-def build_workloads(torch, g4, gen, W):
+def build_prefill(torch, g4, gen, c):
+    """Raw (pre-prologue) inputs and output buffers of one prefill workload."""
     dev = "cuda"
-    st = {}
-
-    # ---- 31B sliding prefill
-    c = W["31b_sliding_prefill"]
     q_raw = gen.normal_bf16((c.B, c.S, c.Hq, c.D), gen.seed_key(c.cfg_id, gen.Q), dev)
-    k_raw = gen.normal_bf16((c.B, c.S, c.Hkv, c.D), gen.seed_key(c.cfg_id, gen.K), dev)
-    v_raw = gen.normal_bf16((c.B, c.S, c.Hkv, c.D), gen.seed_key(c.cfg_id, gen.V), dev)
     wq = gen.norm_weight(c.D, gen.seed_key(c.cfg_id, gen.WQ)).to(dev)
     wk = gen.norm_weight(c.D, gen.seed_key(c.cfg_id, gen.WK)).to(dev)
-    desc = g4.layer_desc(c.Hq, c.Hkv, c.D, window=c.window, rotary_dims=c.rotary_dims, rope_theta=c.theta)
-    st["sliding"] = dict(c=c, desc=desc, q_raw=q_raw, k_raw=k_raw, v_raw=v_raw, wq=wq, wk=wk,
-                         q=torch.empty_like(q_raw), k=torch.empty_like(k_raw), v=torch.empty_like(v_raw),
-                         out=torch.empty_like(q_raw))
-
-    # ---- 31B global prefill, K=V
-    c = W["31b_global_kv_prefill"]
-    q_raw = gen.normal_bf16((c.B, c.S, c.Hq, c.D), gen.seed_key(c.cfg_id, gen.Q), dev)
-    X = gen.normal_bf16((c.B, c.S, c.Hkv, c.D), gen.seed_key(c.cfg_id, gen.X), dev)
-    wq = gen.norm_weight(c.D, gen.seed_key(c.cfg_id, gen.WQ)).to(dev)
-    wk = gen.norm_weight(c.D, gen.seed_key(c.cfg_id, gen.WK)).to(dev)
-    desc = g4.layer_desc(c.Hq, c.Hkv, c.D, window=0, k_eq_v=True, rotary_dims=c.rotary_dims,
+    desc = g4.layer_desc(c.Hq, c.Hkv, c.D, window=c.window, k_eq_v=c.k_eq_v, rotary_dims=c.rotary_dims,
                          rope_theta=c.theta)
-    ws = torch.empty(g4.g4attn_prefill_workspace_bytes(desc, c.B, c.S), dtype=torch.uint8, device=dev)
-    st["global"] = dict(c=c, desc=desc, q_raw=q_raw, X=X, wq=wq, wk=wk, q=torch.empty_like(q_raw),
-                        out=torch.empty_like(q_raw), ws=ws)
+    s = dict(c=c, desc=desc, q_raw=q_raw, wq=wq, wk=wk, q=torch.empty_like(q_raw), out=torch.empty_like(q_raw))
+    if c.k_eq_v:
+        s["X"] = gen.normal_bf16((c.B, c.S, c.Hkv, c.D), gen.seed_key(c.cfg_id, gen.X), dev)
+        s["ws"] = torch.empty(g4.g4attn_prefill_workspace_bytes(desc, c.B, c.S), dtype=torch.uint8, device=dev)
+    else:
+        s["k_raw"] = gen.normal_bf16((c.B, c.S, c.Hkv, c.D), gen.seed_key(c.cfg_id, gen.K), dev)
+        s["v_raw"] = gen.normal_bf16((c.B, c.S, c.Hkv, c.D), gen.seed_key(c.cfg_id, gen.V), dev)
+        s["k"] = torch.empty_like(s["k_raw"])
+        s["v"] = torch.empty_like(s["v_raw"])
+        s["ws"] = torch.empty(g4.g4attn_prefill_workspace_bytes(desc, c.B, c.S), dtype=torch.uint8, device=dev)
+    return s
 
-    # ---- 31B global decode, K=V cache
-    c = W["31b_global_kv_decode"]
+
+def build_decode(torch, g4, gen, c):
+    """KV cache (K=V, pre-normed and roped rows), raw queries and buffers of the decode workload."""
+    dev = "cuda"
     L = gen.decode_lengths(c.B, c.len_lo, c.len_hi, gen.seed_key(c.cfg_id, gen.LENS))
     n = L.astype(np.int64) + 1            # the new token's own row is slot L_b
     cap = c.cache_cap
@@ -109,10 +103,16 @@ def build_workloads(torch, g4, gen, W):
     kv_len = torch.from_numpy(n.astype(np.int32)).to(dev)
     max_len = int(n.max())
     dws = torch.empty(g4.g4attn_decode_workspace_bytes(desc, c.B, max_len, 0), dtype=torch.uint8, device=dev)
-    st["decode"] = dict(c=c, desc=desc, cache=cache, q_raw=q_raw, wq=wq, pos0=pos0, kv_len=kv_len,
-                        max_len=max_len, max_pos=int(L.max()), n=n, q=torch.empty((c.B, 1, c.Hq, c.D),
-                        dtype=torch.bfloat16, device=dev), out=torch.empty((c.B, c.Hq, c.D),
-                        dtype=torch.bfloat16, device=dev), ws=dws)
+    return dict(c=c, desc=desc, cache=cache, q_raw=q_raw, wq=wq, pos0=pos0, kv_len=kv_len, L=L,
+                max_len=max_len, max_pos=int(L.max()), n=n,
+                q=torch.empty((c.B, 1, c.Hq, c.D), dtype=torch.bfloat16, device=dev),
+                out=torch.empty((c.B, c.Hq, c.D), dtype=torch.bfloat16, device=dev), ws=dws)
+
+
+def build_workloads(torch, g4, gen, W):
+    st = {"sliding": build_prefill(torch, g4, gen, W["31b_sliding_prefill"]),
+          "global": build_prefill(torch, g4, gen, W["31b_global_kv_prefill"]),
+          "decode": build_decode(torch, g4, gen, W["31b_global_kv_decode"])}
     torch.cuda.synchronize()
     return st
 
@@ -125,7 +125,19 @@ def run_sliding(g4, s):
 
 
 def run_sliding_attn(g4, s):
-    g4.g4attn_prefill(s["desc"], s["q"], s["k"], s["v"], s["out"])
+    g4.g4attn_prefill(s["desc"], s["q"], s["k"], s["v"], s["out"], workspace=s["ws"])
+
+
+def run_prefill(g4, s, lse=None):
+    """The whole prefill hot path of one workload: prologue(s) + attention."""
+    c = s["c"]
+    g4.g4attn_norm_rope(s["q_raw"], s["q"], s["wq"], c.D, c.rotary_dims, c.theta)
+    if c.k_eq_v:
+        g4.g4attn_prefill(s["desc"], s["q"], s["X"], None, s["out"], w_k=s["wk"], lse=lse, workspace=s["ws"])
+    else:
+        g4.g4attn_norm_rope(s["k_raw"], s["k"], s["wk"], c.D, c.rotary_dims, c.theta)
+        g4.g4attn_norm_rope(s["v_raw"], s["v"], None, c.D, 0, c.theta)
+        g4.g4attn_prefill(s["desc"], s["q"], s["k"], s["v"], s["out"], lse=lse, workspace=s["ws"])
 
 
 def run_global_pro(g4, s):

@@ -1,0 +1,134 @@
+"""Parity at the full workload sizes, in the launch configuration bench.py times.
+
+Each test builds one workload with the bench's own builders (same seeded
+generators, shapes and buffers), runs the whole hot path the way the bench
+does (prologue kernels + attention), and compares sampled outputs with the
+fp64 oracle computed one row (or one decode head) at a time from the raw
+bf16 inputs.  The sampled rows cover the first and last tokens, tile and
+window edges and seeded random positions in every KV group.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import bench
+from g4inputs import WORKLOADS, gen
+from oracle import norm_rope as onr
+
+from tests._cmp import assert_parity
+
+pytestmark = pytest.mark.gpu
+
+f64 = gen.to_f64
+
+# The prologue hands q and k to attention as bf16 (half-ulp 2^-9 relative),
+# while the oracle keeps them in fp64, so each logit scale * q.k moves by up
+# to about 2^-8 |scale q.k|: 0.01 for the largest logits here (about 2.5 in
+# magnitude for RMS-normalised rows with N(1, 0.1) weights and random
+# directions, up to ~4 in the tails).  The log-sum-exp is a weighted mean of
+# the logits' errors, so it gets the same bound.
+LSE_ATOL = 1e-2
+
+
+def _sample_tokens(S, window, n_rand, seed):
+    """First/last tokens, 32-key tile edges, window edges and seeded random positions."""
+    fixed = {0, 1, 31, 32, 33, 127, 128, S // 2, S - 2, S - 1}
+    if window:
+        fixed |= {window - 1, window, window + 1, min(S - 1, 2 * window + 5)}
+    rng = np.random.default_rng(seed)
+    rand = set(rng.integers(0, S, size=n_rand).tolist())
+    return np.array(sorted(t for t in fixed | rand if 0 <= t < S), dtype=np.int64)
+
+
+def _prefill_oracle_rows(s, b, g, toks, heads):
+    """Oracle out [len(toks), len(heads), D] and lse for batch b, KV group g."""
+    c = s["c"]
+    hi = int(toks.max()) + 1
+    lo = 0 if c.window == 0 else max(0, int(toks.min()) - c.window + 1)
+    pos_k = np.arange(lo, hi)[None, :]
+    if c.k_eq_v:
+        X = f64(s["X"][b:b + 1, lo:hi, g:g + 1])
+        K, V = onr.kv_tied_k_v(X, f64(s["wk"]), pos_k, c.rotary_dims, c.theta)
+    else:
+        K = onr.norm_rope(f64(s["k_raw"][b:b + 1, lo:hi, g:g + 1]), f64(s["wk"]), pos_k, c.rotary_dims, c.theta)
+        V = onr.norm_rope(f64(s["v_raw"][b:b + 1, lo:hi, g:g + 1]), None, pos_k, 0, c.theta)
+    out = np.zeros((len(toks), len(heads), c.D))
+    lse = np.zeros((len(toks), len(heads)))
+    for ti, t in enumerate(toks):
+        qraw = f64(s["q_raw"][b:b + 1, t:t + 1, heads])                 # [1, 1, H, D]
+        q = onr.norm_rope(qraw, f64(s["wq"]), np.array([[t]]), c.rotary_dims, c.theta)
+        k0 = 0 if c.window == 0 else max(0, int(t) - c.window + 1)
+        kk = K[0, k0 - lo:t + 1 - lo, 0]                                 # visible keys of row t
+        vv = V[0, k0 - lo:t + 1 - lo, 0]
+        for hi_, _ in enumerate(heads):
+            sc = c.scale * (kk @ q[0, 0, hi_])
+            m = sc.max()
+            e = np.exp(sc - m)
+            out[ti, hi_] = (e @ vv) / e.sum()
+            lse[ti, hi_] = m + np.log(e.sum())
+    return out, lse
+
+
+@pytest.mark.parametrize("name", ["e2b_sliding_prefill", "e2b_global_prefill", "31b_sliding_prefill",
+                                  "31b_global_kv_prefill"])
+def test_full_size_prefill_sampled_rows(gpu_lib, name):
+    g4 = gpu_lib
+    c = WORKLOADS[name]
+    s = bench.build_prefill(torch, g4, gen, c)
+    lse = torch.empty((c.B, c.Hq, c.S), dtype=torch.float32, device="cuda")
+    bench.run_prefill(g4, s, lse=lse)
+    torch.cuda.synchronize()
+    G = c.Hq // c.Hkv
+    got_all, ref_all = [], []
+    for b in range(c.B):
+        for g in range(c.Hkv):
+            toks = _sample_tokens(c.S, c.window, n_rand=6 if c.Hkv > 4 else 12, seed=(c.cfg_id, b, g))
+            # two query heads of the group: the first and the last
+            heads = sorted({g * G, g * G + G - 1})
+            ro, rl = _prefill_oracle_rows(s, b, g, toks, heads)
+            ti = torch.as_tensor(toks, device="cuda")
+            hi = torch.as_tensor(heads, device="cuda")
+            got = f64(s["out"][b].index_select(0, ti).index_select(1, hi))
+            got_lse = lse[b].index_select(0, hi).index_select(1, ti).T.cpu().numpy()
+            np.testing.assert_allclose(got_lse, rl, rtol=0, atol=LSE_ATOL,
+                                       err_msg=f"{name} b={b} g={g} lse")
+            got_all.append(got)
+            ref_all.append(ro)
+    assert_parity(np.concatenate([x.reshape(-1) for x in got_all]),
+                  np.concatenate([x.reshape(-1) for x in ref_all]), f"{name} sampled rows")
+
+
+def test_full_size_decode_sampled_heads(gpu_lib):
+    g4 = gpu_lib
+    c = WORKLOADS["31b_global_kv_decode"]
+    s = bench.build_decode(torch, g4, gen, c)
+    lse = torch.empty((c.B, c.Hq), dtype=torch.float32, device="cuda")
+    bench.run_decode_pro(g4, s)
+    g4.g4attn_decode(s["desc"], s["q"].view(c.B, c.Hq, c.D), s["cache"], s["cache"], s["kv_len"], s["max_len"],
+                     s["out"], lse=lse, workspace=s["ws"])
+    torch.cuda.synchronize()
+    L, n = s["L"], s["n"]
+    # the shortest and the longest sequence plus two seeded others; 8 heads each
+    order = np.argsort(n)
+    rng = np.random.default_rng(55)
+    batch = sorted({int(order[0]), int(order[-1])} | set(rng.choice(c.B, size=2, replace=False).tolist()))
+    heads = [0, 3, 4, 7, 8, 15, 16, 31]
+    G = c.Hq // c.Hkv
+    got, ref = [], []
+    for b in batch:
+        q = onr.norm_rope(f64(s["q_raw"][b:b + 1]), f64(s["wq"]), np.array([[L[b]]]), c.rotary_dims, c.theta)
+        rows = {}
+        for h in heads:
+            g = h // G
+            if g not in rows:
+                rows = {g: f64(s["cache"][b, g, :int(n[b])])}   # one group's rows at a time
+            kk = rows[g]
+            sc = c.scale * (kk @ q[0, 0, h])
+            m = sc.max()
+            e = np.exp(sc - m)
+            ref.append((e @ kk) / e.sum())
+            got.append(f64(s["out"][b, h]))
+            np.testing.assert_allclose(float(lse[b, h]), m + np.log(e.sum()), rtol=0, atol=LSE_ATOL,
+                                       err_msg=f"decode b={b} h={h} lse")
+    assert_parity(np.stack(got), np.stack(ref), "31B decode sampled heads")
