@@ -33,6 +33,32 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 
+# HBM bytes per launch of the K=V prefill main kernel from two rocprofv3
+# counter runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what
+# the counter reads for a plain 1 GiB copy (x2.00 fetch, x1.00 write).  Valid
+# only for the kernel sources they were taken on (hash below): once those
+# change, the roofline reports traffic as null until the counters are re-taken.
+PREFILL_TRAFFIC = {
+    "sources": ["prefill.hip", "g4attn_internal.h", "norm_rope.hip", "abi.hip"],
+    "sources_sha256": "1bc99a2ccdcbe3c169aeaef4967c86d798a278f5c10d56890aee655d72d0e89d",
+    "fetch_kib": 3.24633e6, "fetch_scale": 2.0,
+    "write_kib": 2.04194e6, "write_scale": 1.0,
+}
+
+
+def measured_traffic():
+    """Scaled HBM bytes per launch of the K=V prefill kernel, or None if its sources changed."""
+    import hashlib
+    csrc = os.path.join(ROOT, "decoder_attention_g4attn_amd", "csrc")
+    h = hashlib.sha256()
+    for f in PREFILL_TRAFFIC["sources"]:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != PREFILL_TRAFFIC["sources_sha256"]:
+        return None
+    t = PREFILL_TRAFFIC
+    return (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024.0
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -282,7 +308,8 @@ def main():
     if "global_attn" in avg:
         ach = res["global_prefill_tflops"]
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
+                "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
                 "kernel": "g4attn_prefill on the 31B K=V global layer (K=V pre-pass + prefill_kernel<512,K=V>)",
                 "flops_per_launch": fl_global}
     out = {

@@ -141,8 +141,10 @@ size_t g4attn_prefill_workspace_bytes(const g4attn_layer_desc* desc, int32_t B, 
  *   workspace  >= g4attn_prefill_workspace_bytes(desc, B, S) bytes, 16-byte
  *              aligned (per-row softmax maxima and flags; for K=V also the
  *              inverse RMS and rotated slice of each key row).
- * Requires S >= 1, B >= 1.  Window and causality are applied exactly
- * (integer logic); rows never see keys past themselves.
+ * Requires S >= 1, B >= 1, and a K/V row stride kv_strides[1] below 2^25
+ * elements (G4ATTN_ERR_UNSUPPORTED otherwise: a 32-key tile's row offsets are
+ * formed in 32 bits).  Window and causality are applied exactly (integer
+ * logic); rows never see keys past themselves.
  */
 g4attn_status g4attn_prefill(const g4attn_layer_desc* desc, const g4attn_bf16* q,
                              const g4attn_bf16* k, const g4attn_bf16* v, const g4attn_bf16* w_k,
