@@ -596,6 +596,202 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   }
 }
 
+// D = 256 without K=V, two waves per SIMD (8 per CU, two workgroups).  With
+// 256 registers a wave has room for O (128, AGPRs), Q^T (64) and one score
+// tile, but not for the software pipeline of prefill_kernel; instead the
+// second wave on each SIMD runs its MFMAs while this one does its softmax,
+// copies and barrier.  Two LDS stages (70 KiB per workgroup); the tile loop
+// is the plain one: copy tile kt+1, S = K Q^T, softmax, O += V^T P^T.
+// Same rows, layouts, masks, fixed-reference softmax and recompute launch as
+// prefill_kernel.
+template <bool REDO>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_d256_kernel(PrefillArgs a) {
+  constexpr int D = 256;
+  typedef Cfg<D, false> C;
+  constexpr int L2 = 2;  // LDS operand reads issued ahead of their MFMA
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE];
+  const uint32_t lds0 = lds_addr((G4_LDS void*)smem);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int hh = lane >> 5;
+  const int lr = lane & 31;
+  const int G = a.Hq / a.Hkv;
+  const int ntiles = (int)(((int64_t)a.S * G + kBM - 1) / kBM);
+  int b, g, tile;
+  wg_map(ntiles, a.Hkv, b, g, tile);
+
+  const int64_t F0 = (int64_t)tile * kBM;
+  const int64_t Flast = min(F0 + kBM - 1, (int64_t)a.S * G - 1);
+  const int tq0 = (int)(F0 / G), tq1 = (int)(Flast / G);
+  const int64_t F = F0 + wave * 32 + lr;
+  const int tq = (int)(F / G);
+  const int head = g * G + (int)(F % G);
+  const bool valid = tq < a.S;
+
+  const int kt_lo = a.window ? max(0, tq0 - a.window + 1) / kBN : 0;
+  const int kt_hi = tq1 / kBN;
+  int* wg_flags = a.flags + (((int64_t)b * a.Hkv + g) * ntiles + tile) * kWaves;
+  if (REDO) {
+    if ((wg_flags[0] | wg_flags[1] | wg_flags[2] | wg_flags[3]) == 0) return;
+  }
+
+  load_tile<D, false>(a, lds0, kt_lo, b, g, wave, lane);
+
+  bf16x8 qf[C::NT];
+  {
+    const uint16_t* qrow = a.q + b * a.qs[0] + (int64_t)min(tq, a.S - 1) * a.qs[1] + head * a.qs[2];
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t) qf[t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * t + 8 * hh));
+  }
+
+  const int k_x = kv_xor<D>(lr);
+  const uint32_t koff0 = kv_row_off<D>(lr) + 16 * (hh ^ k_x);
+  const uint32_t koff1 = kv_row_off<D>(lr) + 16 * ((2 + hh) ^ k_x);
+  const int tG = lane >> 4, te = (lane >> 2) & 3, tqd = lane & 3;
+  const int tr_row0 = 4 * (tG >> 1) + te;
+  const int tr_chunk = 2 * (tG & 1) + (tqd >> 1);
+  int toff[2][2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int R = 16 * m + 8 * u + tr_row0;
+      toff[m][u] = C::KT_BYTES + kv_row_off<D>(R) + (tqd & 1) * 8 + 16 * (tr_chunk ^ kv_xor<D>(R));
+    }
+  auto lds_ptr = [&](int so) { return (const G4_LDS char*)smem + so; };
+
+  const float cs = a.scale_log2;
+  const uint32_t w_eff = a.window ? (uint32_t)a.window : 0x7fffffffu;
+  auto edge_tile = [&](int kt) {
+    const int key0 = kt * kBN;
+    return !((key0 + kBN - 1 <= tq0) && (a.window == 0 || key0 >= tq1 - a.window + 1));
+  };
+  auto visible = [&](int kt, int r) {
+    const uint32_t d = (uint32_t)(tq - 4 * hh - kt * kBN) - (uint32_t)(8 * (r >> 2) + (r & 3));
+    return d < w_eff;
+  };
+  auto tile_max = [&](const f32x16& s, int kt) {
+    const bool edge = edge_tile(kt);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, ((!edge) | visible(kt, r)) ? s[r] * cs : -INFINITY);
+    return mx;
+  };
+  auto qk = [&](int so) -> f32x16 {
+    bf16x8 ka[L2 + 1];
+    auto kread = [&](int t) {
+      return lds_read_b128(lds_ptr(so) + ((t & 1) ? koff1 : koff0) + 64 * (t >> 1));
+    };
+#pragma unroll
+    for (int t = 0; t < L2; ++t) ka[t] = kread(t);
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t) {
+      if (t + L2 < C::NT) ka[(t + L2) % (L2 + 1)] = kread(t + L2);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % (L2 + 1)], qf[t], s, 0, 0, 0);
+    }
+    return s;
+  };
+
+  float m_ref = -INFINITY;
+  float l_part[4] = {0.f, 0.f, 0.f, 0.f};
+  if (REDO) {
+    float m_run = -INFINITY;
+    int so = 0;
+    for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+      wait_vmem_all();
+      __syncthreads();
+      if (kt < kt_hi) load_tile<D, false>(a, lds0 + (C::STAGE - so), kt + 1, b, g, wave, lane);
+      m_run = fmaxf(m_run, tile_max(qk(so), kt));
+      so = C::STAGE - so;
+    }
+    m_ref = max_xor32(m_run);
+    __syncthreads();
+    load_tile<D, false>(a, lds0, kt_lo, b, g, wave, lane);
+  }
+
+  f32x16 oacc[C::NC];
+#pragma unroll
+  for (int c = 0; c < C::NC; ++c) oacc[c] = f32x16{};
+  int so = 0;
+  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+    wait_vmem_all();  // this wave's copies of tile kt have landed
+    __syncthreads();  // all of tile kt is in LDS; every wave is done with tile kt-1
+    if (kt < kt_hi) load_tile<D, false>(a, lds0 + (C::STAGE - so), kt + 1, b, g, wave, lane);
+    f32x16 s = qk(so);
+    if (!REDO && __builtin_amdgcn_ballot_w64(m_ref == -INFINITY)) {
+      const float rowmx = max_xor32(tile_max(s, kt));
+      m_ref = m_ref == -INFINITY ? rowmx : m_ref;
+    }
+    if (edge_tile(kt)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = visible(kt, r) ? s[r] : a.mask_s;
+    }
+    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+      u32x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r0 = 8 * mm + 2 * i;
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r0], cs, -m_use));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r0 + 1], cs, -m_use));
+        l_part[i] += p0 + p1;
+        w[i] = pack_bf2(p0, p1);
+      }
+      pb[mm] = __builtin_bit_cast(bf16x8, w);
+    }
+    constexpr int NPV = 2 * C::NC;
+    auto vread = [&](int i) -> bf16x8 {
+      const int mm = i / C::NC, cb = i % C::NC;
+      const i16x4 lo = lds_read_tr16(lds_ptr(so) + toff[mm][0] + 64 * cb);
+      const i16x4 hi = lds_read_tr16(lds_ptr(so) + toff[mm][1] + 64 * cb);
+      return cat_tr(lo, hi);
+    };
+    bf16x8 va[L2 + 1];
+#pragma unroll
+    for (int i = 0; i < L2; ++i) va[i] = vread(i);
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      if (i + L2 < NPV) va[(i + L2) % (L2 + 1)] = vread(i + L2);
+      const int mm = i / C::NC, cb = i % C::NC;
+      if (cb == 0)
+        mfma_acc<true>(oacc[cb], va[i % (L2 + 1)], pb[mm]);
+      else
+        mfma_acc<false>(oacc[cb], va[i % (L2 + 1)], pb[mm]);
+    }
+    so = C::STAGE - so;
+  }
+  asm volatile("s_nop 15\n\ts_nop 1"
+               : "+a"(oacc[0]), "+a"(oacc[1]), "+a"(oacc[2]), "+a"(oacc[3]), "+a"(oacc[4]), "+a"(oacc[5]),
+                 "+a"(oacc[6]), "+a"(oacc[7]));
+
+  const float l_tot = sum_xor32((l_part[0] + l_part[1]) + (l_part[2] + l_part[3]));
+  if (!REDO) {
+    const bool over = valid && !(l_tot <= 0x1p64f);
+    if (lane == 0) wg_flags[wave] = __builtin_amdgcn_ballot_w64(over) != 0;
+  }
+  if (!valid) return;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  uint16_t* orow = a.out + b * a.os[0] + (int64_t)tq * a.os[1] + head * a.os[2];
+#pragma unroll
+  for (int c = 0; c < C::NC; ++c) {
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      u32x2 w;
+      w[0] = pack_bf2(oacc[c][4 * gq + 0] * inv, oacc[c][4 * gq + 1] * inv);
+      w[1] = pack_bf2(oacc[c][4 * gq + 2] * inv, oacc[c][4 * gq + 3] * inv);
+      *(u32x2*)(orow + 32 * c + 8 * gq + 4 * hh) = w;
+    }
+  }
+  if (a.lse && hh == 0) {
+    a.lse[((int64_t)b * a.Hq + head) * a.S + tq] =
+        l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
@@ -610,8 +806,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
       hipLaunchKernelGGL((redo ? prefill_kernel<512, false, true> : prefill_kernel<512, false, false>), grid,
                          dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((redo ? prefill_kernel<256, false, true> : prefill_kernel<256, false, false>), grid,
-                         dim3(256), 0, st, a);
+      hipLaunchKernelGGL((redo ? prefill_d256_kernel<true> : prefill_d256_kernel<false>), grid, dim3(256), 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
