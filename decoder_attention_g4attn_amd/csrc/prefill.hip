@@ -596,19 +596,22 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   }
 }
 
-// D = 256 without K=V, two waves per SIMD (8 per CU, two workgroups).  With
-// 256 registers a wave has room for O (128, AGPRs), Q^T (64) and one score
-// tile, but not for the software pipeline of prefill_kernel; instead the
-// second wave on each SIMD runs its MFMAs while this one does its softmax,
-// copies and barrier.  Two LDS stages (70 KiB per workgroup); the tile loop
-// is the plain one: copy tile kt+1, S = K Q^T, softmax, O += V^T P^T.
-// Same rows, layouts, masks, fixed-reference softmax and recompute launch as
-// prefill_kernel.
-template <bool REDO>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// D = 256 without K=V, two waves per SIMD.  With 256 registers a wave has
+// room for O (128, AGPRs), Q^T (64) and one score tile, but not for the
+// software pipeline of prefill_kernel; instead the second wave on each SIMD
+// runs its MFMAs while this one does its softmax, copies and barrier.  A
+// workgroup of NW waves owns 32 NW rows; with NW = 4 two workgroups share a
+// CU, so one can run while the other waits at its barrier (NW = 8, one per
+// CU, copies each K/V tile for twice the rows but measured slower).  Two LDS
+// stages (70 KiB); the tile loop is the plain one: copy tile kt+1, S = K Q^T,
+// softmax, O += V^T P^T.  Same layouts, masks, fixed-reference softmax and
+// recompute launch as prefill_kernel.
+template <int NW, bool REDO>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_d256_kernel(PrefillArgs a) {
   constexpr int D = 256;
   typedef Cfg<D, false> C;
+  constexpr int BM = 32 * NW;  // rows per workgroup
   constexpr int L2 = 2;  // LDS operand reads issued ahead of their MFMA
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE];
   const uint32_t lds0 = lds_addr((G4_LDS void*)smem);
@@ -617,12 +620,12 @@ void prefill_d256_kernel(PrefillArgs a) {
   const int hh = lane >> 5;
   const int lr = lane & 31;
   const int G = a.Hq / a.Hkv;
-  const int ntiles = (int)(((int64_t)a.S * G + kBM - 1) / kBM);
+  const int ntiles = (int)(((int64_t)a.S * G + BM - 1) / BM);
   int b, g, tile;
   wg_map(ntiles, a.Hkv, b, g, tile);
 
-  const int64_t F0 = (int64_t)tile * kBM;
-  const int64_t Flast = min(F0 + kBM - 1, (int64_t)a.S * G - 1);
+  const int64_t F0 = (int64_t)tile * BM;
+  const int64_t Flast = min(F0 + BM - 1, (int64_t)a.S * G - 1);
   const int tq0 = (int)(F0 / G), tq1 = (int)(Flast / G);
   const int64_t F = F0 + wave * 32 + lr;
   const int tq = (int)(F / G);
@@ -631,12 +634,32 @@ void prefill_d256_kernel(PrefillArgs a) {
 
   const int kt_lo = a.window ? max(0, tq0 - a.window + 1) / kBN : 0;
   const int kt_hi = tq1 / kBN;
-  int* wg_flags = a.flags + (((int64_t)b * a.Hkv + g) * ntiles + tile) * kWaves;
+  int* wg_flags = a.flags + (((int64_t)b * a.Hkv + g) * ntiles + tile) * NW;
   if (REDO) {
-    if ((wg_flags[0] | wg_flags[1] | wg_flags[2] | wg_flags[3]) == 0) return;
+    int any = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) any |= wg_flags[w];
+    if (any == 0) return;
   }
 
-  load_tile<D, false>(a, lds0, kt_lo, b, g, wave, lane);
+  // Copy of key tile kt: each of the NW waves copies 16/NW row pairs of K
+  // and of V (lanes 0..31 row s, lanes 32..63 row s + 16); rows past S
+  // re-read row S-1 (masked).
+  auto load_tile_w = [&](uint32_t stage, int kt) {
+    const TileSrc ts = tile_src<D, false>(a, kt, b, g);
+    const uint32_t rs = (uint32_t)(a.ks[1] * 2);
+#pragma unroll
+    for (int which = 0; which < 2; ++which)
+#pragma unroll
+      for (int i = 0; i < 16 / NW; ++i) {
+        const int s = wave * (16 / NW) + i;
+        const uint32_t r0 = min((uint32_t)s * rs, ts.last_off);
+        const uint32_t r1 = min((uint32_t)(s + 16) * rs, ts.last_off);
+        const uint32_t off = ((lane >> 5) ? r1 : r0) + (uint32_t)((lane & 31) ^ kv_xor<D>(s)) * 16u;
+        g2lds16s(which ? ts.v : ts.k, off, stage + which * C::KT_BYTES + s * kSeg);
+      }
+  };
+  load_tile_w(lds0, kt_lo);
 
   bf16x8 qf[C::NT];
   {
@@ -702,13 +725,13 @@ void prefill_d256_kernel(PrefillArgs a) {
     for (int kt = kt_lo; kt <= kt_hi; ++kt) {
       wait_vmem_all();
       __syncthreads();
-      if (kt < kt_hi) load_tile<D, false>(a, lds0 + (C::STAGE - so), kt + 1, b, g, wave, lane);
+      if (kt < kt_hi) load_tile_w(lds0 + (C::STAGE - so), kt + 1);
       m_run = fmaxf(m_run, tile_max(qk(so), kt));
       so = C::STAGE - so;
     }
     m_ref = max_xor32(m_run);
     __syncthreads();
-    load_tile<D, false>(a, lds0, kt_lo, b, g, wave, lane);
+    load_tile_w(lds0, kt_lo);
   }
 
   f32x16 oacc[C::NC];
@@ -718,7 +741,7 @@ void prefill_d256_kernel(PrefillArgs a) {
   for (int kt = kt_lo; kt <= kt_hi; ++kt) {
     wait_vmem_all();  // this wave's copies of tile kt have landed
     __syncthreads();  // all of tile kt is in LDS; every wave is done with tile kt-1
-    if (kt < kt_hi) load_tile<D, false>(a, lds0 + (C::STAGE - so), kt + 1, b, g, wave, lane);
+    if (kt < kt_hi) load_tile_w(lds0 + (C::STAGE - so), kt + 1);
     f32x16 s = qk(so);
     if (!REDO && __builtin_amdgcn_ballot_w64(m_ref == -INFINITY)) {
       const float rowmx = max_xor32(tile_max(s, kt));
@@ -798,6 +821,9 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
   const int64_t ntiles = ((int64_t)a.S * G + kBM - 1) / kBM;
   const dim3 grid((unsigned)ntiles, (unsigned)a.Hkv, (unsigned)a.B);
+  constexpr int kNW256 = 4;  // waves per workgroup of the D = 256 kernel (8: slower, one workgroup per CU)
+  const dim3 grid256((unsigned)(((int64_t)a.S * G + 32 * kNW256 - 1) / (32 * kNW256)), (unsigned)a.Hkv,
+                     (unsigned)a.B);
   for (int redo = 0; redo < 2; ++redo) {
     if (a.kv_tied)
       hipLaunchKernelGGL((redo ? prefill_kernel<512, true, true> : prefill_kernel<512, true, false>),
@@ -806,7 +832,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
       hipLaunchKernelGGL((redo ? prefill_kernel<512, false, true> : prefill_kernel<512, false, false>), grid,
                          dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((redo ? prefill_d256_kernel<true> : prefill_d256_kernel<false>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((redo ? prefill_d256_kernel<kNW256, true> : prefill_d256_kernel<kNW256, false>), grid256,
+                         dim3(64 * kNW256), 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
