@@ -14,8 +14,9 @@ inputs resident in HBM:
 
 Prints one JSON line.  ``value`` is the prefill attention throughput
 (algorithmic flops = 4*D per visible (row, key) pair per query head, over
-both prefill calls); the decode stream rate, per-stage timings, the roofline
-of the dominant kernel and the CPU oracle baseline are in the same line.
+both prefill calls); the decode stream rate, per-stage timings (median over
+the timed steps, which every rate uses, and min), the roofline of the
+dominant kernel and the CPU oracle baseline are in the same line.
 """
 
 import argparse
@@ -63,7 +64,7 @@ def measured_traffic():
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["sliding", "global", "decode"], default=None,
@@ -285,7 +286,9 @@ def main():
     for evs in all_evs:
         for name, e0, e1 in evs:
             ms.setdefault(name, []).append(e0.elapsed_time(e1))
-    avg = {k: float(np.mean(v)) for k, v in ms.items()}
+    # per-stage median over the timed steps drives every rate; min is reported beside it
+    avg = {k: float(np.median(v)) for k, v in ms.items()}
+    mins = {k: float(np.min(v)) for k, v in ms.items()}
 
     cs, cg, cd = st["sliding"]["c"], st["global"]["c"], st["decode"]["c"]
     fl_sliding = 4.0 * cs.D * g4.visible_pairs(cs.S, cs.window) * cs.Hq * cs.B
@@ -332,6 +335,7 @@ def main():
         "sliding_prefill_tflops": round(res.get("sliding_prefill_tflops", 0.0), 2) if "sliding_prefill_tflops" in res else None,
         "global_prefill_tflops": round(res.get("global_prefill_tflops", 0.0), 2) if "global_prefill_tflops" in res else None,
         "stage_ms": {k: round(v, 4) for k, v in avg.items()},
+        "stage_ms_min": {k: round(v, 4) for k, v in mins.items()},
         "roofline": roof,
     }
     if not args.no_cpu_baseline and "global_attn" in avg:
