@@ -67,7 +67,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["sliding", "global", "decode"], default=None,
+    ap.add_argument("--only", choices=["sliding", "global", "decode", "sdecode"], default=None,
                     help="time one stage only (profiling aid)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device-to-device copy 3 times (HBM-counter calibration)")
@@ -115,23 +115,33 @@ def build_prefill(torch, g4, gen, c):
 
 
 def build_decode(torch, g4, gen, c):
-    """KV cache (K=V, pre-normed and roped rows), raw queries and buffers of the decode workload."""
+    """KV cache(s) of post-prologue rows, raw queries and buffers of a decode workload.
+
+    Global K=V layer: one cache [B, Hkv, cap, D] holds rows 0..L_b (the new
+    token's own row is slot L_b).  Sliding layer: separate K and V rolling
+    caches of `window` slots holding the last min(L_b + 1, window) positions
+    (position p in slot p mod window; every slot once L_b + 1 >= window).
+    """
     dev = "cuda"
     L = gen.decode_lengths(c.B, c.len_lo, c.len_hi, gen.seed_key(c.cfg_id, gen.LENS))
-    n = L.astype(np.int64) + 1            # the new token's own row is slot L_b
+    n = L.astype(np.int64) + 1            # positions so far, the new token included
     cap = c.cache_cap
-    cache = torch.empty((c.B, c.Hkv, cap, c.D), dtype=torch.bfloat16, device=dev)
-    for b in range(c.B):
-        cache[b, :, :n[b]] = gen.normal_bf16((c.Hkv, int(n[b]), c.D), gen.seed_key(c.cfg_id, gen.CACHE, b), dev)
+    rows = np.minimum(n, cap) if c.window else n
+    caches = []
+    for which in ((gen.CACHE,) if c.k_eq_v else (gen.CACHE, gen.CACHE_V)):
+        cache = torch.empty((c.B, c.Hkv, cap, c.D), dtype=torch.bfloat16, device=dev)
+        for b in range(c.B):
+            cache[b, :, :rows[b]] = gen.normal_bf16((c.Hkv, int(rows[b]), c.D), gen.seed_key(c.cfg_id, which, b), dev)
+        caches.append(cache)
     q_raw = gen.normal_bf16((c.B, 1, c.Hq, c.D), gen.seed_key(c.cfg_id, gen.QDEC), dev)
     wq = gen.norm_weight(c.D, gen.seed_key(c.cfg_id, gen.WQ)).to(dev)
-    desc = g4.layer_desc(c.Hq, c.Hkv, c.D, window=0, rotary_dims=c.rotary_dims, rope_theta=c.theta)
+    desc = g4.layer_desc(c.Hq, c.Hkv, c.D, window=c.window, rotary_dims=c.rotary_dims, rope_theta=c.theta)
     pos0 = torch.from_numpy(L.astype(np.int32)).to(dev)
     kv_len = torch.from_numpy(n.astype(np.int32)).to(dev)
     max_len = int(n.max())
     dws = torch.empty(g4.g4attn_decode_workspace_bytes(desc, c.B, max_len, 0), dtype=torch.uint8, device=dev)
-    return dict(c=c, desc=desc, cache=cache, q_raw=q_raw, wq=wq, pos0=pos0, kv_len=kv_len, L=L,
-                max_len=max_len, max_pos=int(L.max()), n=n,
+    return dict(c=c, desc=desc, cache=caches[0], vcache=caches[-1], q_raw=q_raw, wq=wq, pos0=pos0,
+                kv_len=kv_len, L=L, max_len=max_len, max_pos=int(L.max()), n=n, rows=rows,
                 q=torch.empty((c.B, 1, c.Hq, c.D), dtype=torch.bfloat16, device=dev),
                 out=torch.empty((c.B, c.Hq, c.D), dtype=torch.bfloat16, device=dev), ws=dws)
 
@@ -139,7 +149,8 @@ def build_decode(torch, g4, gen, c):
 def build_workloads(torch, g4, gen, W):
     st = {"sliding": build_prefill(torch, g4, gen, W["31b_sliding_prefill"]),
           "global": build_prefill(torch, g4, gen, W["31b_global_kv_prefill"]),
-          "decode": build_decode(torch, g4, gen, W["31b_global_kv_decode"])}
+          "decode": build_decode(torch, g4, gen, W["31b_global_kv_decode"]),
+          "sdecode": build_decode(torch, g4, gen, W["31b_sliding_decode"])}
     torch.cuda.synchronize()
     return st
 
@@ -184,7 +195,7 @@ def run_decode_pro(g4, s):
 
 def run_decode_attn(g4, s):
     g4.g4attn_decode(s["desc"], s["q"].view(s["q"].shape[0], s["q"].shape[2], s["q"].shape[3]),
-                     s["cache"], s["cache"], s["kv_len"], s["max_len"], s["out"], workspace=s["ws"])
+                     s["cache"], s["vcache"], s["kv_len"], s["max_len"], s["out"], workspace=s["ws"])
 
 
 def cpu_baseline(torch, gen, st, budget_s=15.0):
@@ -253,7 +264,9 @@ def main():
 
     plan = [("sliding_prologue", run_sliding, "sliding"), ("sliding_attn", run_sliding_attn, "sliding"),
             ("global_prologue", run_global_pro, "global"), ("global_attn", run_global_attn, "global"),
-            ("decode_prologue", run_decode_pro, "decode"), ("decode_attn", run_decode_attn, "decode")]
+            ("decode_prologue", run_decode_pro, "decode"), ("decode_attn", run_decode_attn, "decode"),
+            ("sliding_decode_prologue", run_decode_pro, "sdecode"),
+            ("sliding_decode_attn", run_decode_attn, "sdecode")]
     if args.only:
         plan = [p for p in plan if p[2] == args.only]
 
@@ -295,6 +308,9 @@ def main():
     fl_global = 4.0 * cg.D * g4.visible_pairs(cg.S, 0) * cg.Hq * cg.B
     dec = st["decode"]
     dec_bytes = float(dec["n"].sum()) * cd.Hkv * cd.D * 2 + 2.0 * cd.B * cd.Hq * cd.D * 2
+    sdec, csd = st["sdecode"], st["sdecode"]["c"]
+    # separate K and V rings: 2 * D bytes per row per KV head for each
+    sdec_bytes = float(sdec["rows"].sum()) * csd.Hkv * csd.D * 2 * 2 + 2.0 * csd.B * csd.Hq * csd.D * 2
     res = {}
     if "sliding_attn" in avg:
         res["sliding_prefill_tflops"] = fl_sliding / avg["sliding_attn"] / 1e9
@@ -302,6 +318,8 @@ def main():
         res["global_prefill_tflops"] = fl_global / avg["global_attn"] / 1e9
     if "decode_attn" in avg:
         res["decode_GBps"] = dec_bytes / avg["decode_attn"] / 1e6
+    if "sliding_decode_attn" in avg:
+        res["sliding_decode_GBps"] = sdec_bytes / avg["sliding_decode_attn"] / 1e6
     prefill_ms = avg.get("sliding_attn", 0.0) + avg.get("global_attn", 0.0)
     prefill_fl = (fl_sliding if "sliding_attn" in avg else 0) + (fl_global if "global_attn" in avg else 0)
     value = prefill_fl / prefill_ms / 1e9 if prefill_ms > 0 else None
@@ -332,6 +350,7 @@ def main():
         },
         "decode_GBps": round(res.get("decode_GBps", 0.0), 1) if "decode_GBps" in res else None,
         "decode_hbm_frac": round(res["decode_GBps"] / PEAK_HBM_GBPS, 4) if "decode_GBps" in res else None,
+        "sliding_decode_GBps": round(res["sliding_decode_GBps"], 1) if "sliding_decode_GBps" in res else None,
         "sliding_prefill_tflops": round(res.get("sliding_prefill_tflops", 0.0), 2) if "sliding_prefill_tflops" in res else None,
         "global_prefill_tflops": round(res.get("global_prefill_tflops", 0.0), 2) if "global_prefill_tflops" in res else None,
         "stage_ms": {k: round(v, 4) for k, v in avg.items()},

@@ -78,7 +78,7 @@ def load(path=None):
     lib.g4attn_norm_rope.restype = ctypes.c_int
     lib.g4attn_norm_rope.argtypes = [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_float,
-                                     _P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P]
+                                     _P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P]
     lib.g4attn_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.g4attn_prefill_workspace_bytes.argtypes = [ctypes.POINTER(LayerDesc), ctypes.c_int32, ctypes.c_int32]
     lib.g4attn_prefill.restype = ctypes.c_int
@@ -132,11 +132,12 @@ def _raise(status, where):
 
 # --------------------------------------------------------------- entry points
 def g4attn_norm_rope(x, y, weight, head_dim, rotary_dims, rope_theta, rms_eps=1e-6,
-                     pos0=None, max_pos=None, cache_cap=0, stream=None):
+                     pos0=None, max_pos=None, cache_cap=0, ring=False, stream=None):
     """y = RoPE(RMSNorm(x) * weight) for x [B, S, H, D]; see g4attn_norm_rope in g4attn.h.
 
     ``cache_cap > 0``: ``y`` is a cache ``[B, H, cache_cap, D]`` written at rows
-    ``pos0[b] + t``.  ``pos0`` is an int32 device tensor ``[B]`` or None.
+    ``pos0[b] + t`` (``ring``: at rows ``(pos0[b] + t) % cache_cap``, a sliding
+    layer's rolling cache).  ``pos0`` is an int32 device tensor ``[B]`` or None.
     """
     lib = load()
     _check_bf16(x, y, weight)
@@ -146,7 +147,7 @@ def g4attn_norm_rope(x, y, weight, head_dim, rotary_dims, rope_theta, rms_eps=1e
     if max_pos is None:
         max_pos = S - 1 if pos0 is None else int(pos0.max().item()) + S - 1
     st = lib.g4attn_norm_rope(_ptr(x), _ptr(y), _ptr(weight), B, S, H, head_dim, rotary_dims,
-                              rope_theta, rms_eps, xs, ys, _ptr(pos0), max_pos, cache_cap,
+                              rope_theta, rms_eps, xs, ys, _ptr(pos0), max_pos, cache_cap, int(bool(ring)),
                               _stream(stream))
     _raise(st, "g4attn_norm_rope")
     return y
@@ -186,7 +187,8 @@ def g4attn_decode(desc, q, k_cache, v_cache, kv_len, max_kv_len, out, lse=None, 
     """Split-KV decode; see g4attn_decode in g4attn.h.  Returns ``out``.
 
     ``q`` [B, Hq, D], caches [B, Hkv, cap, D] (``v_cache`` may be ``k_cache``),
-    ``kv_len`` int32 device tensor [B].
+    ``kv_len`` int32 device tensor [B].  Sliding layers (``desc.window > 0``)
+    read a ring cache of ``cap == window`` slots (see g4attn_norm_rope's ring).
     """
     lib = load()
     _check_bf16(q, k_cache, v_cache, out)

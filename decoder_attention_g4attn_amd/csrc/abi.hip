@@ -14,7 +14,7 @@ namespace {
 
 thread_local int32_t t_last_hip_error = 0;
 
-constexpr int32_t kVersion = 100;  // 0.1.0
+constexpr int32_t kVersion = 200;  // 0.2.0: ring caches (sliding-layer decode)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -94,10 +94,11 @@ g4attn_status g4attn_norm_rope(const g4attn_bf16* x, g4attn_bf16* y, const g4att
                                int32_t rotary_dims, float rope_theta, float rms_eps,
                                const int64_t x_strides[3], const int64_t y_strides[3],
                                const int32_t* pos0, int32_t max_pos, int32_t y_cache_cap,
-                               void* stream) {
+                               int32_t y_cache_ring, void* stream) {
   if (!x || !y || !x_strides) return G4ATTN_ERR_NULL;
   if (y_cache_cap == 0 && !y_strides) return G4ATTN_ERR_NULL;
   if (B < 1 || S < 1 || H < 1 || B > 65535 || y_cache_cap < 0) return G4ATTN_ERR_SHAPE;
+  if (y_cache_ring != 0 && (y_cache_ring != 1 || y_cache_cap == 0)) return G4ATTN_ERR_SHAPE;
   if (!head_dim_ok(head_dim) || !rot_ok(head_dim, rotary_dims)) return G4ATTN_ERR_UNSUPPORTED;
   if (!(rope_theta > 0.f) || !isfinite(rope_theta) || !(rms_eps >= 0.f) || !isfinite(rms_eps))
     return G4ATTN_ERR_SHAPE;
@@ -105,7 +106,7 @@ g4attn_status g4attn_norm_rope(const g4attn_bf16* x, g4attn_bf16* y, const g4att
   if (!strides_ok(x_strides) || (y_cache_cap == 0 && !strides_ok(y_strides))) return G4ATTN_ERR_LAYOUT;
   const int64_t top = pos0 ? (int64_t)max_pos : (int64_t)S - 1;
   if (pos0 && max_pos < S - 1) return G4ATTN_ERR_SHAPE;
-  if (y_cache_cap > 0 && top >= y_cache_cap) return G4ATTN_ERR_CACHE_OVERFLOW;
+  if (y_cache_cap > 0 && !y_cache_ring && top >= y_cache_cap) return G4ATTN_ERR_CACHE_OVERFLOW;
 
   g4attn::NormRopeArgs a{};
   a.x = x; a.y = y; a.w = weight;
@@ -118,6 +119,7 @@ g4attn_status g4attn_norm_rope(const g4attn_bf16* x, g4attn_bf16* y, const g4att
   }
   a.pos0 = pos0;
   a.cache_cap = y_cache_cap;
+  a.ring = y_cache_ring;
   return hip_status(g4attn::launch_norm_rope(a, (hipStream_t)stream));
 }
 
@@ -213,13 +215,20 @@ g4attn_status g4attn_prefill(const g4attn_layer_desc* d, const g4attn_bf16* q,
   return hip_status(g4attn::launch_prefill(a, s));
 }
 
+// Cache rows a decode reads at most: sliding layers keep the last `window`
+// positions in a ring of that many slots, so min(kv_len, window) of them.
+static int32_t decode_rows(const g4attn_layer_desc* d, int32_t max_kv_len) {
+  return d->window > 0 ? (max_kv_len < d->window ? max_kv_len : d->window) : max_kv_len;
+}
+
 size_t g4attn_decode_workspace_bytes(const g4attn_layer_desc* d, int32_t B, int32_t max_kv_len,
                                      int32_t num_splits) {
   if (!d || B < 1 || max_kv_len < 1 || num_splits < 0 || d->num_kv_heads < 1 || d->num_q_heads < 1 ||
       !head_dim_ok(d->head_dim))
     return 0;
-  const int64_t c = decode_chunk(d, B, max_kv_len, num_splits);
-  const int64_t ns = ((int64_t)max_kv_len + c - 1) / c;
+  const int32_t rows = decode_rows(d, max_kv_len);
+  const int64_t c = decode_chunk(d, B, rows, num_splits);
+  const int64_t ns = ((int64_t)rows + c - 1) / c;
   const size_t ph = (size_t)B * d->num_q_heads;
   const size_t pg = (size_t)B * d->num_kv_heads;
   return align256(ph * ns * d->head_dim * sizeof(float)) + 2 * align256(ph * ns * sizeof(float)) +
@@ -234,15 +243,17 @@ g4attn_status g4attn_decode(const g4attn_layer_desc* d, const g4attn_bf16* q,
   g4attn_status st = desc_check(d);
   if (st != G4ATTN_OK) return st;
   if (!q || !k_cache || !v_cache || !kv_len || !out) return G4ATTN_ERR_NULL;
-  if (d->window != 0) return G4ATTN_ERR_UNSUPPORTED;          // sliding-window decode not built
   if (d->num_q_heads / d->num_kv_heads > 16) return G4ATTN_ERR_UNSUPPORTED;
   if (B < 1 || B > 65535 || max_kv_len < 1 || cache_cap < 1 || num_splits < 0) return G4ATTN_ERR_SHAPE;
-  if (max_kv_len > cache_cap) return G4ATTN_ERR_CACHE_OVERFLOW;
+  // sliding layer: the cache is a ring of exactly `window` slots
+  if (d->window != 0 && cache_cap != d->window) return G4ATTN_ERR_SHAPE;
+  if (d->window == 0 && max_kv_len > cache_cap) return G4ATTN_ERR_CACHE_OVERFLOW;
+  const int32_t rows = decode_rows(d, max_kv_len);
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
       (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
     return G4ATTN_ERR_LAYOUT;
-  const int64_t c = decode_chunk(d, B, max_kv_len, num_splits);
-  const int64_t ns = ((int64_t)max_kv_len + c - 1) / c;
+  const int64_t c = decode_chunk(d, B, rows, num_splits);
+  const int64_t ns = ((int64_t)rows + c - 1) / c;
   if (ns > 65535) return G4ATTN_ERR_SHAPE;
   const size_t need = g4attn_decode_workspace_bytes(d, B, max_kv_len, num_splits);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return G4ATTN_ERR_WORKSPACE;
@@ -259,7 +270,7 @@ g4attn_status g4attn_decode(const g4attn_layer_desc* d, const g4attn_bf16* q,
   wsp += align256(ph * ns * sizeof(float));
   a.dflags = (int*)wsp;
   a.B = B; a.Hq = d->num_q_heads; a.Hkv = d->num_kv_heads; a.D = d->head_dim; a.cap = cache_cap;
-  a.nsplit = (int)ns; a.chunk = (int)c; a.max_len = max_kv_len;
+  a.nsplit = (int)ns; a.chunk = (int)c; a.max_len = rows;  // kv_len is clamped to rows in the kernel
   a.scale_log2 = d->scale * g4attn::kLog2e;
   return hip_status(g4attn::launch_decode(a, (hipStream_t)stream));
 }

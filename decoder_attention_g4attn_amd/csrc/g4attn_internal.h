@@ -130,6 +130,7 @@ struct NormRopeArgs {
   int64_t xs[3], ys[3];
   const int32_t* pos0;
   int cache_cap;
+  int ring;                 // cache mode: row p mod cache_cap instead of row p
 };
 hipError_t launch_norm_rope(const NormRopeArgs& a, hipStream_t st);
 

@@ -85,7 +85,11 @@ __global__ __launch_bounds__(256) void norm_rope_kernel(NormRopeArgs a) {
     for (int e = 0; e < E; ++e) { wl[e] = 1.f; wh[e] = 1.f; }
   }
   const bool cache = a.cache_cap > 0;
-  if (cache && (p < 0 || p >= a.cache_cap)) return;
+  // linear cache: row p, p in [0, cap); ring: row p mod cap, and of the S
+  // new positions only the last cap are kept (earlier ones would be
+  // overwritten within this call).
+  if (cache && (p < 0 || (a.ring ? t < a.S - a.cache_cap : p >= a.cache_cap))) return;
+  const int row = cache && a.ring ? p % a.cache_cap : p;
 
   for (int h = 0; h < a.H; ++h) {
     const uint16_t* xr = a.x + b * a.xs[0] + t * a.xs[1] + h * a.xs[2];
@@ -110,7 +114,7 @@ __global__ __launch_bounds__(256) void norm_rope_kernel(NormRopeArgs a) {
         yhi[e] = v;
       }
     }
-    uint16_t* yr = cache ? a.y + (((int64_t)b * a.H + h) * a.cache_cap + p) * D
+    uint16_t* yr = cache ? a.y + (((int64_t)b * a.H + h) * a.cache_cap + row) * D
                          : a.y + b * a.ys[0] + t * a.ys[1] + h * a.ys[2];
     Vec<E>::store(yr + j0, ylo);
     Vec<E>::store(yr + HALF + j0, yhi);
@@ -118,7 +122,8 @@ __global__ __launch_bounds__(256) void norm_rope_kernel(NormRopeArgs a) {
 }
 
 // K=V pre-pass on the raw tied projection X (D = 512, 128 rotated dims):
-//   r[b,g,t]      = 1 / sqrt(mean_d X^2 + eps)
+//   r[b,g,t]      = rscale / sqrt(mean_d X^2 + eps)   (the inverse RMS, with
+//                   the logit scale folded in by the caller)
 //   krot[b,g,t,:] = RoPE_t(X * w_k) on dims 0..63 and 256..319 (no r)
 // so that the attention kernel can form K = r * RoPE(X * w_k) and V = r * X
 // from one tile of X (see prefill.hip).

@@ -41,8 +41,9 @@ class Workload:
 
     @property
     def cache_cap(self):
-        # Room for the longest cache plus the new token's own slot.
-        return self.len_hi + 1
+        # Global layer: room for the longest cache plus the new token's own
+        # slot.  Sliding layer: a rolling cache of `window` slots.
+        return self.window if self.window else self.len_hi + 1
 
 
 WORKLOADS = {
@@ -61,6 +62,11 @@ WORKLOADS = {
     "31b_global_kv_decode": Workload(
         "31b_global_kv_decode", 5, "decode", B=32, S=1, Hq=32, Hkv=4, D=512,
         window=0, rotary_dims=128, theta=1e6, k_eq_v=True,
+        len_lo=32768, len_hi=131072),
+    # sliding-layer decode of the same 31B batch over rolling caches
+    "31b_sliding_decode": Workload(
+        "31b_sliding_decode", 6, "decode", B=32, S=1, Hq=32, Hkv=16, D=256,
+        window=1024, rotary_dims=256, theta=1e4, k_eq_v=False,
         len_lo=32768, len_hi=131072),
 }
 

@@ -16,7 +16,7 @@ import numpy as np
 import torch
 
 # tensor ids
-Q, K, V, X, WQ, WK, CACHE, QDEC, LENS = range(9)
+Q, K, V, X, WQ, WK, CACHE, QDEC, LENS, CACHE_V = range(10)  # CACHE_V: separate V cache
 
 
 def seed_key(cfg_id, tensor_id, chunk=0, seed=0):

@@ -93,16 +93,23 @@ typedef struct {
  *   y          y_cache_cap == 0: [B, S, H, D] with strides y_strides;
  *              y_cache_cap  > 0: a contiguous cache [B, H, y_cache_cap, D];
  *              row p of sequence b, head h receives the result
- *              (y_strides ignored).
+ *              (y_strides ignored), or with y_cache_ring = 1 row
+ *              p mod y_cache_cap: the rolling cache of a sliding layer,
+ *              which keeps the last y_cache_cap (= window) positions
+ *              (gemma4-pt-claude README, "KV Cache": window-sized caches on
+ *              sliding layers).  Of the S positions of one call only the
+ *              last y_cache_cap are written (the earlier ones would be
+ *              overwritten by them).
  *   weight     [D] bf16 or NULL (weightless; the V-norm).
  *   head_dim   256 or 512; rotary_dims in {0, head_dim/4, head_dim}.
  *   pos0       device int32 [B] (first position of each sequence) or NULL
  *              (positions start at 0).
  *   max_pos    host-known upper bound of every p (pos0[b] + S - 1); required
- *              >= S - 1.  In cache mode max_pos >= y_cache_cap is
+ *              >= S - 1.  In (linear) cache mode max_pos >= y_cache_cap is
  *              G4ATTN_ERR_CACHE_OVERFLOW (the cache raises rather than
  *              evicting: gemma4-pt-claude README, "KV Cache").  The kernel
  *              also skips any row outside [0, y_cache_cap).
+ *   y_cache_ring  0 or 1 (1 needs y_cache_cap > 0), else G4ATTN_ERR_SHAPE.
  * x and y may not overlap unless x == y with equal strides (in place).
  */
 g4attn_status g4attn_norm_rope(const g4attn_bf16* x, g4attn_bf16* y, const g4attn_bf16* weight,
@@ -110,7 +117,7 @@ g4attn_status g4attn_norm_rope(const g4attn_bf16* x, g4attn_bf16* y, const g4att
                                int32_t rotary_dims, float rope_theta, float rms_eps,
                                const int64_t x_strides[3], const int64_t y_strides[3],
                                const int32_t* pos0, int32_t max_pos, int32_t y_cache_cap,
-                               void* stream);
+                               int32_t y_cache_ring, void* stream);
 
 /* Workspace (bytes) that g4attn_prefill needs for this layer and size. */
 size_t g4attn_prefill_workspace_bytes(const g4attn_layer_desc* desc, int32_t B, int32_t S);
@@ -153,34 +160,45 @@ g4attn_status g4attn_prefill(const g4attn_layer_desc* desc, const g4attn_bf16* q
                              const int64_t o_strides[3], void* workspace, size_t workspace_bytes,
                              void* stream);
 
-/* Workspace (bytes) that g4attn_decode needs; num_splits as passed to it. */
+/* Workspace (bytes) that g4attn_decode needs; num_splits as passed to it
+ * (a sliding layer's size depends on min(max_kv_len, window) only). */
 size_t g4attn_decode_workspace_bytes(const g4attn_layer_desc* desc, int32_t B,
                                      int32_t max_kv_len, int32_t num_splits);
 
 /*
  * Single-token decode over a KV cache (vinija.ai primer, "KV cache and
- * long-context scaling"; gemma4-pt-claude README, "KV Cache"):
+ * long-context scaling" and "Sliding-window attention"; gemma4-pt-claude
+ * README, "KV Cache"):
  *
  *   out[b,h] = sum_{j < n_b} softmax_j(scale * q[b,h] . K[b,g,j]) V[b,g,j],
  *   lse[b,h] = log sum_{j < n_b} exp(scale * q[b,h] . K[b,g,j]),
- *   g = h / (Hq/Hkv),  n_b = kv_len[b]
+ *   g = h / (Hq/Hkv),  n_b = kv_len[b] (global) or min(kv_len[b], window)
+ *   (sliding: j runs over the filled slots of the ring)
  *
  *   q          [B, Hq, D] contiguous post-prologue queries (norm + RoPE at
  *              the new token's position, e.g. via g4attn_norm_rope).
  *   k_cache    [B, Hkv, cache_cap, D] contiguous post-prologue keys.
  *   v_cache    same shape; may equal k_cache (one tensor serves as both).
- *   kv_len     device int32 [B]; each value in [1, max_kv_len] (rows past a
- *              sequence's n_b are never read).
- *   max_kv_len host-known bound of kv_len; > cache_cap is
- *              G4ATTN_ERR_CACHE_OVERFLOW.
+ *   kv_len     device int32 [B]; each value in [1, max_kv_len]: the number of
+ *              positions of the sequence so far, the new token included.
+ *              Global layer (window == 0): rows [0, kv_len[b]) are read,
+ *              rows past them never.  Sliding layer (window > 0): k_cache and
+ *              v_cache are rings of cache_cap == window slots (position p in
+ *              slot p mod window, as g4attn_norm_rope's ring mode writes
+ *              them), and the min(kv_len[b], window) filled slots, which hold
+ *              exactly the positions the new token sees, are read (softmax
+ *              does not depend on their order).
+ *   max_kv_len host-known bound of kv_len; global layer: > cache_cap is
+ *              G4ATTN_ERR_CACHE_OVERFLOW; sliding layer: cache_cap != window
+ *              is G4ATTN_ERR_SHAPE.
  *   out        [B, Hq, D] bf16 contiguous;  lse  [B, Hq] fp32 or NULL.
- *   num_splits 0 = automatic; otherwise the KV range [0, max_kv_len) is cut
- *              into num_splits equal chunks (a multiple of 64 rows each);
- *              the partial results are merged by a log-sum-exp combine.
+ *   num_splits 0 = automatic; otherwise the row range [0, rows) is cut into
+ *              num_splits equal chunks (a multiple of 64 rows each), with
+ *              rows = max_kv_len (global) or min(max_kv_len, window)
+ *              (sliding); the partial results are merged by a log-sum-exp
+ *              combine.
  *   workspace  >= g4attn_decode_workspace_bytes(desc, B, max_kv_len,
  *              num_splits) bytes, 16-byte aligned.
- * Valid for window == 0 only (sliding-window decode is not built:
- * G4ATTN_ERR_UNSUPPORTED).
  */
 g4attn_status g4attn_decode(const g4attn_layer_desc* desc, const g4attn_bf16* q,
                             const g4attn_bf16* k_cache, const g4attn_bf16* v_cache,

@@ -24,6 +24,10 @@ Sources
 * Decode over a KV cache: the new query attends over the stored keys and
   values of every earlier token [vinija.ai Gemma 4 primer, "KV cache and
   long-context scaling"; gemma4-pt-claude README, "KV Cache"].
+* Sliding layers keep a window-sized cache [gemma4-pt-claude README, "KV
+  Cache": sliding-layer caches hold the window, global ones grow]; decoding
+  past the window must agree with the uncached forward pass [same page,
+  "Tests" list].
 
 Readings where the pages are silent or disagree
 -----------------------------------------------
@@ -39,6 +43,8 @@ Readings where the pages are silent or disagree
 * Decode: the cache holds post-prologue keys and values; the query attends
   over the first ``n_b`` rows of its sequence's cache (``n_b`` includes the
   new token's own slot).
+* Rolling cache of a sliding layer: ``w`` slots, position ``p`` stored in
+  slot ``p mod w`` (each write replaces the position ``w`` earlier).
 
 Pins (tests/test_oracle_attention.py)
 -------------------------------------
@@ -51,6 +57,10 @@ Pins (tests/test_oracle_attention.py)
   ``w = 1`` gives ``out = v``; ``S <= w`` equals the global result; a
   scale of 0 gives ``lse = log(count)``; decode of the last row equals the
   prefill row.
+* Rolling cache: the slot contents after sequential writes against the
+  closed form ``p = L - ((L - s) mod w)``; decode over the ring equals the
+  sliding prefill's row ``L`` (the uncached forward) for lengths below, at
+  and far past the window.
 """
 
 import numpy as np
@@ -216,3 +226,45 @@ def _pairs_closed(S, window):
     if S <= w:
         return S * (S + 1) // 2
     return w * (w + 1) // 2 + (S - w) * w
+
+
+def ring_positions(n, window):
+    """Position held by each slot of a ``window``-slot rolling cache after
+    positions ``0 .. n-1`` were written in order (slot ``p mod window``);
+    -1 for a slot never written."""
+    pos = np.full(window, -1, dtype=np.int64)
+    for p in range(int(n)):
+        pos[p % window] = p
+    return pos
+
+
+def sliding_decode_ring(q, k_ring, v_ring, n, scale, window):
+    """Single-token decode of a sliding layer over rolling caches.
+
+    ``q``: ``[B, Hq, D]`` (the new token at position ``n[b] - 1``);
+    ``k_ring``, ``v_ring``: ``[B, Hkv, window, D]`` with position ``p`` in
+    slot ``p mod window``; ``n``: ``[B]`` positions so far, the new token
+    included.  The query sees the slots whose position ``p`` satisfies
+    ``0 <= (n[b] - 1) - p < window``.  Returns ``(out [B, Hq, D], lse [B, Hq])``.
+    """
+    Bq, Hq, D = q.shape
+    Hkv = k_ring.shape[1]
+    out = np.zeros((Bq, Hq, D))
+    lse = np.full((Bq, Hq), -np.inf)
+    for b in range(Bq):
+        pos = ring_positions(n[b], window)
+        last = int(n[b]) - 1
+        vis = [s for s in range(window) if pos[s] >= 0 and visible(last, int(pos[s]), window)]
+        if not vis:
+            continue
+        for h in range(Hq):
+            g = _kv_head(h, Hq, Hkv)
+            kk = np.asarray(k_ring[b, g, vis, :], np.float64)
+            vv = np.asarray(v_ring[b, g, vis, :], np.float64)
+            sc = scale * (kk @ np.asarray(q[b, h], np.float64))
+            mx = np.max(sc)
+            e = np.exp(sc - mx)
+            den = np.sum(e)
+            out[b, h] = (e @ vv) / den
+            lse[b, h] = mx + np.log(den)
+    return out, lse

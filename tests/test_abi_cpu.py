@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert g4.g4attn_version() == 100
+    assert g4.g4attn_version() == 200
     for s in range(8):
         assert g4.g4attn_status_str(s)
     assert g4.load().g4attn_last_hip_error() == 0
@@ -93,7 +93,8 @@ def test_decode_validation():
     assert _decode(_desc(), q=None) == g4.ERR_NULL
     assert _decode(_desc(), kl=None) == g4.ERR_NULL
     assert _decode(_desc(), max_len=129, cap=128) == g4.ERR_CACHE_OVERFLOW    # cache overflow raises
-    assert _decode(_desc(window=1024)) == g4.ERR_UNSUPPORTED
+    # sliding layer: the cache must be a ring of exactly `window` slots
+    assert _decode(_desc(window=1024)) == g4.ERR_SHAPE
     assert _decode(_desc(num_q_heads=64, num_kv_heads=2)) == g4.ERR_UNSUPPORTED   # > 16 heads per group
     assert _decode(_desc(), max_len=0) == g4.ERR_SHAPE
     assert _decode(_desc(), splits=-1) == g4.ERR_SHAPE
@@ -115,14 +116,22 @@ def test_decode_workspace_sizes():
         assert w == a256(2 * 32 * ns * 512 * 4) + 2 * a256(2 * 32 * ns * 4) + a256(2 * 4 * ns * 4)
 
 
+def test_decode_ring_workspace_uses_window_rows():
+    """A sliding layer's decode reads at most `window` rows of its ring, however long the sequence."""
+    ring = _desc(num_q_heads=32, num_kv_heads=16, head_dim=256, window=1024, rotary_dims=256)
+    glob = _desc(num_q_heads=32, num_kv_heads=16, head_dim=256, window=0, rotary_dims=256)
+    assert g4.g4attn_decode_workspace_bytes(ring, 32, 131073, 0) == g4.g4attn_decode_workspace_bytes(glob, 32, 1024, 0)
+    assert g4.g4attn_decode_workspace_bytes(ring, 32, 700, 3) == g4.g4attn_decode_workspace_bytes(glob, 32, 700, 3)
+
+
 def test_norm_rope_validation():
     lib = g4.load()
     xs = I64(16 * 8 * 256, 8 * 256, 256)
 
     def call(x=FAKE, y=FAKE, B=1, S=16, H=8, D=256, rot=256, theta=1e4, pos0=None, max_pos=15, cap=0,
-             strides=xs):
+             strides=xs, ring=0):
         return lib.g4attn_norm_rope(x, y, None, B, S, H, D, rot, theta, 1e-6, strides, strides, pos0,
-                                    max_pos, cap, None)
+                                    max_pos, cap, ring, None)
 
     assert call(x=None) == g4.ERR_NULL
     assert call(S=0) == g4.ERR_SHAPE
@@ -135,6 +144,9 @@ def test_norm_rope_validation():
     assert call(cap=15) == g4.ERR_CACHE_OVERFLOW
     assert call(pos0=FAKE, max_pos=40, cap=40) == g4.ERR_CACHE_OVERFLOW
     assert call(pos0=FAKE, max_pos=10) == g4.ERR_SHAPE     # max_pos < S - 1
+    # ring mode needs a cache and is a flag
+    assert call(ring=1) == g4.ERR_SHAPE
+    assert call(cap=64, ring=2) == g4.ERR_SHAPE
 
 
 def test_visible_pairs_host_logic_matches_oracle():

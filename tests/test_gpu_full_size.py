@@ -99,36 +99,39 @@ def test_full_size_prefill_sampled_rows(gpu_lib, name):
                   np.concatenate([x.reshape(-1) for x in ref_all]), f"{name} sampled rows")
 
 
-def test_full_size_decode_sampled_heads(gpu_lib):
+@pytest.mark.parametrize("name", ["31b_global_kv_decode", "31b_sliding_decode"])
+def test_full_size_decode_sampled_heads(gpu_lib, name):
     g4 = gpu_lib
-    c = WORKLOADS["31b_global_kv_decode"]
+    c = WORKLOADS[name]
     s = bench.build_decode(torch, g4, gen, c)
     lse = torch.empty((c.B, c.Hq), dtype=torch.float32, device="cuda")
     bench.run_decode_pro(g4, s)
-    g4.g4attn_decode(s["desc"], s["q"].view(c.B, c.Hq, c.D), s["cache"], s["cache"], s["kv_len"], s["max_len"],
+    g4.g4attn_decode(s["desc"], s["q"].view(c.B, c.Hq, c.D), s["cache"], s["vcache"], s["kv_len"], s["max_len"],
                      s["out"], lse=lse, workspace=s["ws"])
     torch.cuda.synchronize()
-    L, n = s["L"], s["n"]
-    # the shortest and the longest sequence plus two seeded others; 8 heads each
+    L, n, rows = s["L"], s["n"], s["rows"]
+    # the shortest and the longest sequence plus two seeded others; 8 heads each.
+    # A sliding layer's ring holds min(n, window) rows, all visible to the new token.
     order = np.argsort(n)
     rng = np.random.default_rng(55)
     batch = sorted({int(order[0]), int(order[-1])} | set(rng.choice(c.B, size=2, replace=False).tolist()))
-    heads = [0, 3, 4, 7, 8, 15, 16, 31]
+    heads = [0, 3, 4, 7, 8, 15, 16, 31] if c.Hkv == 4 else [0, 1, 2, 13, 16, 17, 30, 31]
     G = c.Hq // c.Hkv
     got, ref = [], []
     for b in batch:
         q = onr.norm_rope(f64(s["q_raw"][b:b + 1]), f64(s["wq"]), np.array([[L[b]]]), c.rotary_dims, c.theta)
-        rows = {}
+        held = {}
         for h in heads:
             g = h // G
-            if g not in rows:
-                rows = {g: f64(s["cache"][b, g, :int(n[b])])}   # one group's rows at a time
-            kk = rows[g]
+            if g not in held:                                   # one group's rows at a time
+                kk = f64(s["cache"][b, g, :int(rows[b])])
+                held = {g: (kk, kk if c.k_eq_v else f64(s["vcache"][b, g, :int(rows[b])]))}
+            kk, vv = held[g]
             sc = c.scale * (kk @ q[0, 0, h])
             m = sc.max()
             e = np.exp(sc - m)
-            ref.append((e @ kk) / e.sum())
+            ref.append((e @ vv) / e.sum())
             got.append(f64(s["out"][b, h]))
             np.testing.assert_allclose(float(lse[b, h]), m + np.log(e.sum()), rtol=0, atol=LSE_ATOL,
                                        err_msg=f"decode b={b} h={h} lse")
-    assert_parity(np.stack(got), np.stack(ref), "31B decode sampled heads")
+    assert_parity(np.stack(got), np.stack(ref), f"{name} sampled heads")

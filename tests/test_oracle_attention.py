@@ -169,3 +169,49 @@ def test_planted_gqa_mapping_fails_sdpa_pin():
     v2 = v[:, :, [0, 1, 0, 1]]
     bad, _ = at.attention_band(q, k2, v2, 0.3, 0)
     assert not np.allclose(bad, ref, atol=1e-6)
+
+
+@pytest.mark.parametrize("n,w", [(0, 8), (1, 8), (5, 8), (8, 8), (9, 8), (23, 8), (1000, 64), (64, 64)])
+def test_ring_positions_closed_form(n, w):
+    """Sequential writes to slot p mod w leave slot s holding p = L - ((L - s) mod w), L = n - 1."""
+    pos = at.ring_positions(n, w)
+    L = n - 1
+    for s in range(w):
+        want = L - ((L - s) % w) if n > 0 else -1
+        assert pos[s] == (want if want >= 0 else -1)
+    # the slots hold exactly the last min(n, w) positions
+    assert sorted(p for p in pos if p >= 0) == list(range(max(0, n - w), n))
+
+
+@pytest.mark.parametrize("S,w,Hq,Hkv", [(1, 16, 4, 1), (15, 16, 4, 1), (16, 16, 4, 2), (17, 16, 2, 2),
+                                        (53, 16, 4, 2), (200, 32, 8, 1)])
+def test_sliding_decode_ring_equals_uncached_forward(S, w, Hq, Hkv):
+    """Decoding the last token over the rolling caches equals row S-1 of the sliding prefill."""
+    D = 32
+    q, k, v = _qkv(1, S, Hq, Hkv, D)
+    scale = 1.0 / np.sqrt(D)
+    pos = at.ring_positions(S, w)
+    kr = np.full((1, Hkv, w, D), np.nan)
+    vr = np.full((1, Hkv, w, D), np.nan)
+    for s in range(w):
+        if pos[s] >= 0:
+            kr[0, :, s] = k[0, pos[s]]
+            vr[0, :, s] = v[0, pos[s]]
+    o, l_ = at.sliding_decode_ring(q[:, S - 1], kr, vr, np.array([S]), scale, w)
+    ro, rl = at.attention_band(q, k, v, scale, w, rows=np.array([S - 1]))
+    np.testing.assert_allclose(o, ro[:, 0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l_, rl[:, :, 0], rtol=0, atol=1e-12)
+
+
+def test_planted_ring_slot_off_by_one_fails_forward_pin():
+    """A ring that places position p at slot (p + 1) mod w loses the pin against the forward pass."""
+    S, w, D = 40, 16, 32
+    q, k, v = _qkv(1, S, 2, 1, D)
+    kr = np.zeros((1, 1, w, D))
+    vr = np.zeros((1, 1, w, D))
+    for p in range(S - w + 1, S):          # the last w-1 positions, shifted by one slot
+        kr[0, 0, (p + 1) % w] = k[0, p, 0]
+        vr[0, 0, (p + 1) % w] = v[0, p, 0]
+    o, _ = at.sliding_decode_ring(q[:, S - 1], kr, vr, np.array([S]), 1.0 / np.sqrt(D), w)
+    ro, _ = at.attention_band(q, k, v, 1.0 / np.sqrt(D), w, rows=np.array([S - 1]))
+    assert np.abs(o - ro[:, 0]).max() > 1e-3
