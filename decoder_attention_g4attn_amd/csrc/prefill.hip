@@ -233,366 +233,384 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const int lr = lane & 31;   // row within the wave
   const int G = a.Hq / a.Hkv;
   const int ntiles = (int)(((int64_t)a.S * G + kBM - 1) / kBM);
-  int b, g, tile;
-  wg_map(ntiles, a.Hkv, b, g, tile);
-
-  const int64_t F0 = (int64_t)tile * kBM;
-  const int64_t Flast = min(F0 + kBM - 1, (int64_t)a.S * G - 1);
-  const int tq0 = (int)(F0 / G), tq1 = (int)(Flast / G);
-  const int64_t F = F0 + wave * 32 + lr;
-  const int tq = (int)(F / G);
-  const int head = g * G + (int)(F % G);
-  const bool valid = tq < a.S;
-
-  const int kt_lo = a.window ? max(0, tq0 - a.window + 1) / kBN : 0;
-  const int kt_hi = tq1 / kBN;
-  int* wg_flags = a.flags + (((int64_t)b * a.Hkv + g) * ntiles + tile) * kWaves;
-  if (REDO) {
-    if ((wg_flags[0] | wg_flags[1] | wg_flags[2] | wg_flags[3]) == 0) return;
-  }
-
-  // Prefetch the first two tiles, then load this lane's Q^T fragments (rows
-  // past S read row S-1; their results are never stored).  K=V: the K-norm
-  // weight is folded into the non-rotated dims, times qmul.
-  load_tile<D, TIED>(a, lds0, kt_lo, b, g, wave, lane);
-  if (kt_lo < kt_hi) load_tile<D, TIED>(a, lds0 + C::STAGE, kt_lo + 1, b, g, wave, lane);
-
-  bf16x8 qf[C::NT];
-  {
-    const uint16_t* qrow = a.q + b * a.qs[0] + (int64_t)min(tq, a.S - 1) * a.qs[1] + head * a.qs[2];
-    const bool qscale = TIED && a.qmul != 1.f;
+  // Main pass: one workgroup per row tile.  Recompute pass: a small grid of
+  // persistent workgroups walks every row tile and redoes the flagged ones
+  // (most launches find none, and a full grid of early exits costs ~30 us).
+  const int ntotal = ntiles * a.Hkv * a.B;
+  for (int L = REDO ? (int)blockIdx.x : 0;; L += (int)gridDim.x) {
+    int b, g, tile;
+    if (REDO) {
+      if (L >= ntotal) return;
+      tile = L % ntiles;
+      g = (L / ntiles) % a.Hkv;
+      b = L / (ntiles * a.Hkv);
+      const int* fl = a.flags + (((int64_t)b * a.Hkv + g) * ntiles + tile) * kWaves;
+      int any = 0;
 #pragma unroll
-    for (int t = 0; t < C::NT; ++t) {
-      const int d0 = 16 * t + 8 * hh;
-      u32x4 raw = *(const u32x4*)(qrow + d0);
-      if (TIED && !rot_step(t)) {
-        const u32x4 w = *(const u32x4*)(a.w_k + d0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          raw[i] = pack_bf2(bf_lo(raw[i]) * bf_lo(w[i]) * a.qmul, bf_hi(raw[i]) * bf_hi(w[i]) * a.qmul);
-      } else if (qscale) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) raw[i] = pack_bf2(bf_lo(raw[i]) * a.qmul, bf_hi(raw[i]) * a.qmul);
-      }
-      qf[t] = __builtin_bit_cast(bf16x8, raw);
-    }
-  }
-
-  // Per-lane LDS byte offsets within a stage.  QK^T operand (K row lr, dims
-  // 16t + 8hh ..): chunk (2t + hh) ^ x keeps t>>1 in the high bits, so the
-  // address is koff[t & 1] + 64 (t >> 1).
-  const int k_x = kv_xor<D>(lr), kr_x = kr_xor(lr);
-  const uint32_t koff0 = kv_row_off<D>(lr) + 16 * (hh ^ k_x);
-  const uint32_t koff1 = kv_row_off<D>(lr) + 16 * ((2 + hh) ^ k_x);
-  const uint32_t kroff0 = C::KR_OFF + kr_row_off(lr) + 16 * (hh ^ kr_x);
-  const uint32_t kroff1 = C::KR_OFF + kr_row_off(lr) + 16 * ((2 + hh) ^ kr_x);
-  // PV operand (transposing read): issuing lane feeds row 16m + 8u + r0 of
-  // dim block c at 64c + toff[m][u].
-  const int tG = lane >> 4, te = (lane >> 2) & 3, tqd = lane & 3;
-  const int tr_row0 = 4 * (tG >> 1) + te;
-  const int tr_chunk = 2 * (tG & 1) + (tqd >> 1);
-  const int vbase = TIED ? 0 : C::KT_BYTES;
-  int toff[2][2];
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int R = 16 * m + 8 * u + tr_row0;
-      toff[m][u] = vbase + kv_row_off<D>(R) + (tqd & 1) * 8 + 16 * (tr_chunk ^ kv_xor<D>(R));
-    }
-
-  auto lds_ptr = [&](int so) { return (const G4_LDS char*)smem + so; };
-  // K fragment of k-step t of the tile in stage `so` (K=V: rotated k-steps
-  // read the Krot slice, chunk 2u + hh with u = t (t < 4) or t - 12).
-  auto kread = [&](int so, int t) -> bf16x8 {
-    if (TIED && rot_step(t)) {
-      const int u = t < 4 ? t : t - 12;
-      return lds_read_b128(lds_ptr(so) + ((u & 1) ? kroff1 : kroff0) + 64 * (u >> 1));
-    }
-    return lds_read_b128(lds_ptr(so) + ((t & 1) ? koff1 : koff0) + 64 * (t >> 1));
-  };
-
-  // Logit of key slot r in the log2 domain is s[r] * c[r]: c = the key's
-  // inverse RMS times scale*log2(e) (K=V, from the tile) or scale*log2(e).
-  const float cs = a.scale_log2;
-  auto key_mul = [&](int so, float (&c)[16]) {
-    if (TIED) {
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const f32x4 v = *(const G4_LDS f32x4*)(lds_ptr(so) + C::R_OFF + (8 * gq + 4 * hh) * 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) c[4 * gq + i] = v[i];
-      }
+      for (int w = 0; w < kWaves; ++w) any |= fl[w];
+      if (any == 0) continue;  // uniform: every thread reads the same flags
     } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) c[r] = cs;
+      wg_map(ntiles, a.Hkv, b, g, tile);
     }
-  };
-  // Does tile kt need element masks (some key not visible from some row)?
-  auto edge_tile = [&](int kt) {
-    const int key0 = kt * kBN;
-    return !((key0 + kBN - 1 <= tq0) && (a.window == 0 || key0 >= tq1 - a.window + 1));
-  };
-  // Key slot r of tile kt is visible iff 0 <= d < w_eff with d = tq - key:
-  // one unsigned compare (a global layer takes w_eff = 2^31 - 1).
-  const uint32_t w_eff = a.window ? (uint32_t)a.window : 0x7fffffffu;
-  auto visible = [&](int kt, int r) {
-    const uint32_t d = (uint32_t)(tq - 4 * hh - kt * kBN) - (uint32_t)(8 * (r >> 2) + (r & 3));
-    return d < w_eff;
-  };
-  // Maximum logit of this lane's 16 slots of tile kt (-inf if none visible).
-  auto tile_max = [&](const f32x16& s, const float (&c)[16], int kt) {
-    const bool edge = edge_tile(kt);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float x = s[r] * c[r];
-      mx = fmaxf(mx, ((!edge) | visible(kt, r)) ? x : -INFINITY);
-    }
-    return mx;
-  };
 
-  // S^T(tile in stage so) = K Q^T, K reads kLook ahead of their MFMA.
-  auto qk = [&](int so) -> f32x16 {
-    bf16x8 ka[kLook + 1];
-#pragma unroll
-    for (int t = 0; t < kLook; ++t) ka[t] = kread(so, t);
-    f32x16 s = f32x16{};
-#pragma unroll
-    for (int t = 0; t < C::NT; ++t) {
-      if (t + kLook < C::NT) ka[(t + kLook) % (kLook + 1)] = kread(so, t + kLook);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % (kLook + 1)], qf[t], s, 0, 0, 0);
-    }
-    return s;
-  };
+    const int64_t F0 = (int64_t)tile * kBM;
+    const int64_t Flast = min(F0 + kBM - 1, (int64_t)a.S * G - 1);
+    const int tq0 = (int)(F0 / G), tq1 = (int)(Flast / G);
+    const int64_t F = F0 + wave * 32 + lr;
+    const int tq = (int)(F / G);
+    const int head = g * G + (int)(F % G);
+    const bool valid = tq < a.S;
 
-  // Softmax with a fixed per-row reference m_ref (log2 domain): the row's
-  // maximum over its first tile with a visible key; P = exp2(x - m_ref) is
-  // accumulated without ever rescaling O.  Every P is at most the row sum l,
-  // so a row whose l stays <= 2^64 had no overflow risk; a wave with a larger
-  // (or non-finite) l flags its workgroup, which the REDO launch recomputes
-  // with m_ref = the true row maximum (every P <= 1 then).
-  float m_ref = -INFINITY;
-  float l_part[4] = {0.f, 0.f, 0.f, 0.f};  // four partial row sums: no serial add chain
-  // Masked slots of an edge tile: s = mask_s makes s * c = -inf.
-  auto mask_edge = [&](f32x16& s, int kt) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = visible(kt, r) ? s[r] : a.mask_s;
-  };
-  auto first_visible = [&](const f32x16& s, const float (&c)[16], int kt) {
-    if (!REDO && __builtin_amdgcn_ballot_w64(m_ref == -INFINITY)) {  // a row meets its first visible key
-      const float rowmx = max_xor32(tile_max(s, c, kt));
-      m_ref = m_ref == -INFINITY ? rowmx : m_ref;
-    }
-  };
-  // The softmax of one score tile as a list of micro-ops, stage by stage so
-  // that no op waits on the one before it: 16 FMA (x = s c - m), 16 EXP2,
-  // 8 pair sums, 8 row-sum adds, (K=V) 16 multiplies by c, 8 bf16 packs.
-  constexpr int kSmOps = TIED ? 72 : 56;
-  struct Sm {
-    float x[16], ps[8];
-    uint32_t w[8];
-  };
-  // Each op's result is pinned (an empty asm that takes it in and out), so
-  // the op stays in its slot instead of sinking towards the result's use.
-  auto sm_op = [&](Sm& st, const f32x16& s, const float (&c)[16], float m_use, int j) {
-    if (j < 16) {
-      st.x[j] = __builtin_fmaf(s[j], c[j], -m_use);
-      pin(st.x[j]);
-    } else if (j < 32) {
-      st.x[j - 16] = __builtin_amdgcn_exp2f(st.x[j - 16]);
-      pin(st.x[j - 16]);
-    } else if (j < 40) {
-      st.ps[j - 32] = st.x[2 * (j - 32)] + st.x[2 * (j - 32) + 1];
-      pin(st.ps[j - 32]);
-    } else if (j < 48) {
-      l_part[(j - 40) & 3] += st.ps[j - 40];
-      pin(l_part[(j - 40) & 3]);
-    } else if (TIED && j < 64) {
-      st.x[j - 48] *= c[j - 48];
-      pin(st.x[j - 48]);
-    } else {
-      const int i = j - (TIED ? 64 : 48);
-      st.w[i] = pack_bf2(st.x[2 * i], st.x[2 * i + 1]);
-      pin(st.w[i]);
-    }
-  };
-  auto sm_out = [&](const Sm& st, bf16x8 (&pb)[2]) {
-#pragma unroll
-    for (int mm = 0; mm < 2; ++mm) {
-      const u32x4 w = {st.w[4 * mm], st.w[4 * mm + 1], st.w[4 * mm + 2], st.w[4 * mm + 3]};
-      pb[mm] = __builtin_bit_cast(bf16x8, w);
-    }
-  };
-  // P^T operands of score tile s (K=V: P times the key factor).
-  auto softmax = [&](const f32x16& s, const float (&c)[16], bf16x8 (&pb)[2]) {
-    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-    Sm st;
-#pragma unroll
-    for (int j = 0; j < kSmOps; ++j) sm_op(st, s, c, m_use, j);
-    sm_out(st, pb);
-  };
-  // S^T of the tile in stage so, with the softmax of s_prev spread over its
-  // MFMAs: each MFMA is followed by its share of the micro-ops, fenced so the
-  // scheduler keeps this order (the ops run while the MFMA does).
-  // With LOADS, the copy of tile ld_kt into stage ld_so rides along, one
-  // piece after every other MFMA.
-  // ka[0 .. kLook-1] hold the first K fragments, read by the caller.
-  auto qk_softmax = [&](int so, bf16x8 (&ka)[kLook + 1], const f32x16& s_prev, const float (&c)[16],
-                        bf16x8 (&pb)[2], auto loads, int ld_so, int ld_kt) -> f32x16 {
-    constexpr bool LOADS = decltype(loads)::value;
-    const TileSrc ts = tile_src<D, TIED>(a, ld_kt, b, g);
-    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-    Sm st;
-    f32x16 s = f32x16{};
-#pragma unroll
-    for (int t = 0; t < C::NT; ++t) {
-      if (t + kLook < C::NT) ka[(t + kLook) % (kLook + 1)] = kread(so, t + kLook);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % (kLook + 1)], qf[t], s, 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = kSmOps * t / C::NT; j < kSmOps * (t + 1) / C::NT; ++j) sm_op(st, s_prev, c, m_use, j);
-      if (LOADS && (t & 1) == 0 && (t >> 1) < TilePieces<D, TIED>::N)
-        load_piece<D, TIED>(a, ts, lds0 + ld_so, wave, lane, t >> 1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    sm_out(st, pb);
-    return s;
-  };
+    const int kt_lo = a.window ? max(0, tq0 - a.window + 1) / kBN : 0;
+    const int kt_hi = tq1 / kBN;
+    int* wg_flags = a.flags + (((int64_t)b * a.Hkv + g) * ntiles + tile) * kWaves;
 
-  f32x16 oacc[C::NC];
-#pragma unroll
-  for (int c = 0; c < C::NC; ++c) oacc[c] = f32x16{};
-  // O^T += V^T P^T over the tile in stage so, transposing reads kLook ahead.
-  auto pv = [&](int so, const bf16x8 (&pb)[2]) {
-    constexpr int NPV = 2 * C::NC;  // (mm, c) pairs
-    auto vread = [&](int i) -> bf16x8 {
-      const int mm = i / C::NC, c = i % C::NC;
-      const i16x4 lo = lds_read_tr16(lds_ptr(so) + toff[mm][0] + 64 * c);
-      const i16x4 hi = lds_read_tr16(lds_ptr(so) + toff[mm][1] + 64 * c);
-      return cat_tr(lo, hi);
-    };
-    bf16x8 va[kLook + 1];
-#pragma unroll
-    for (int i = 0; i < kLook; ++i) va[i] = vread(i);
-#pragma unroll
-    for (int i = 0; i < NPV; ++i) {
-      if (i + kLook < NPV) va[(i + kLook) % (kLook + 1)] = vread(i + kLook);
-      const int mm = i / C::NC, c = i % C::NC;
-      if (c == 0)
-        mfma_acc<true>(oacc[c], va[i % (kLook + 1)], pb[mm]);
-      else
-        mfma_acc<false>(oacc[c], va[i % (kLook + 1)], pb[mm]);
-    }
-  };
-
-  if (REDO) {
-    // first sweep: the true maximum of every row (stages 0 and 1 hold kt_lo
-    // and kt_lo + 1 already; two-stage ring)
-    float m_run = -INFINITY;
-    int so = 0;
-    for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-      wait_vmem_all();
-      __syncthreads();  // tile kt (and kt + 1) landed; every wave is done with tile kt - 1
-      if (kt > kt_lo && kt < kt_hi) load_tile<D, TIED>(a, lds0 + (C::STAGE - so), kt + 1, b, g, wave, lane);
-      float c[16];
-      key_mul(so, c);
-      const f32x16 s = qk(so);
-      m_run = fmaxf(m_run, tile_max(s, c, kt));
-      so = C::STAGE - so;
-    }
-    m_ref = max_xor32(m_run);
-    __syncthreads();  // every wave is done before the stages are reloaded
+    // Prefetch the first two tiles, then load this lane's Q^T fragments (rows
+    // past S read row S-1; their results are never stored).  K=V: the K-norm
+    // weight is folded into the non-rotated dims, times qmul.
     load_tile<D, TIED>(a, lds0, kt_lo, b, g, wave, lane);
     if (kt_lo < kt_hi) load_tile<D, TIED>(a, lds0 + C::STAGE, kt_lo + 1, b, g, wave, lane);
-  }
 
-  wait_vmem_all();
-  __syncthreads();
-  // One pipeline step: softmax + PV of tile kt (scores s_cur) and the scores
-  // of tile kt + 1 into s_nxt.  Written out twice per loop trip with the two
-  // score registers swapped, so neither is ever copied.
-  int so_cur = 0, so_nxt = C::STAGE, so_ld = NST == 3 ? 2 * C::STAGE : 0;
-  auto step = [&](int kt, f32x16& s_cur, f32x16& s_nxt) {
-    wait_vmem_all();  // this wave's copies of tile kt+1 have landed
-    __syncthreads();  // all of tile kt+1 is in LDS; every wave is done with tile kt-1
-    // first K fragments of tile kt+1 right away: their latency hides under
-    // the bookkeeping below
-    bf16x8 ka[kLook + 1];
+    bf16x8 qf[C::NT];
+    {
+      const uint16_t* qrow = a.q + b * a.qs[0] + (int64_t)min(tq, a.S - 1) * a.qs[1] + head * a.qs[2];
+      const bool qscale = TIED && a.qmul != 1.f;
 #pragma unroll
-    for (int t = 0; t < kLook; ++t) ka[t] = kread(so_nxt, t);
-    float c[16];
-    key_mul(so_cur, c);
-    first_visible(s_cur, c, kt);
-    if (edge_tile(kt)) mask_edge(s_cur, kt);
-    bf16x8 pb[2];
-    // three stages: tile kt+2 goes to the stage tile kt-1 left (past the
-    // end, the last tile is copied again into that unused stage)
-    s_nxt = qk_softmax(so_nxt, ka, s_cur, c, pb, std::integral_constant<bool, NST == 3>{}, so_ld, min(kt + 2, kt_hi));
-    __builtin_amdgcn_sched_barrier(0);
-    pv(so_cur, pb);
-    if (NST == 2 && kt + 2 <= kt_hi) {
-      __syncthreads();  // every wave is done with tile kt
-      load_tile<D, TIED>(a, lds0 + so_cur, kt + 2, b, g, wave, lane);
+      for (int t = 0; t < C::NT; ++t) {
+        const int d0 = 16 * t + 8 * hh;
+        u32x4 raw = *(const u32x4*)(qrow + d0);
+        if (TIED && !rot_step(t)) {
+          const u32x4 w = *(const u32x4*)(a.w_k + d0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            raw[i] = pack_bf2(bf_lo(raw[i]) * bf_lo(w[i]) * a.qmul, bf_hi(raw[i]) * bf_hi(w[i]) * a.qmul);
+        } else if (qscale) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) raw[i] = pack_bf2(bf_lo(raw[i]) * a.qmul, bf_hi(raw[i]) * a.qmul);
+        }
+        qf[t] = __builtin_bit_cast(bf16x8, raw);
+      }
     }
-    const int t = so_cur;
-    so_cur = so_nxt;
-    if (NST == 3) { so_nxt = so_ld; so_ld = t; } else { so_nxt = t; }
-  };
-  auto last = [&](f32x16& s_cur) {
-    float c[16];
-    key_mul(so_cur, c);
-    first_visible(s_cur, c, kt_hi);
-    if (edge_tile(kt_hi)) mask_edge(s_cur, kt_hi);
-    bf16x8 pb[2];
-    softmax(s_cur, c, pb);
-    pv(so_cur, pb);
-  };
-  f32x16 sa = qk(0), sb;
-  int kt = kt_lo;
-  for (; kt + 1 < kt_hi; kt += 2) {
-    step(kt, sa, sb);
-    step(kt + 1, sb, sa);
-  }
-  if (kt < kt_hi) {
-    step(kt, sa, sb);
-    sa = sb;
-  }
-  last(sa);
-  wait_vmem_all();  // the extra copy of the last tile has landed before the wave ends
-  // the last MFMA results are read below: 18 wait states cover an 8-pass XDL
-  asm volatile("s_nop 15\n\ts_nop 1"
-               : "+a"(oacc[0]), "+a"(oacc[1]), "+a"(oacc[2]), "+a"(oacc[3]), "+a"(oacc[4]), "+a"(oacc[5]),
-                 "+a"(oacc[6]), "+a"(oacc[7]));
-  if constexpr (C::NC > 8)
-    asm volatile(""
-                 : "+a"(oacc[8 % C::NC]), "+a"(oacc[9 % C::NC]), "+a"(oacc[10 % C::NC]),
-                   "+a"(oacc[11 % C::NC]), "+a"(oacc[12 % C::NC]), "+a"(oacc[13 % C::NC]),
-                   "+a"(oacc[14 % C::NC]), "+a"(oacc[15 % C::NC]));
 
-  // ---- epilogue: flag, normalise, round once to bf16, store
-  const float l_tot = sum_xor32((l_part[0] + l_part[1]) + (l_part[2] + l_part[3]));
-  if (!REDO) {
-    const bool over = valid && !(l_tot <= 0x1p64f);
-    if (lane == 0) wg_flags[wave] = __builtin_amdgcn_ballot_w64(over) != 0;
-  }
-  if (!valid) return;
-  // K=V: P carried the factor c = r * scale*log2(e) / qmul; omul undoes it.
-  const float inv = l_tot > 0.f ? (TIED ? a.omul : 1.f) / l_tot : 0.f;
-  uint16_t* orow = a.out + b * a.os[0] + (int64_t)tq * a.os[1] + head * a.os[2];
+    // Per-lane LDS byte offsets within a stage.  QK^T operand (K row lr, dims
+    // 16t + 8hh ..): chunk (2t + hh) ^ x keeps t>>1 in the high bits, so the
+    // address is koff[t & 1] + 64 (t >> 1).
+    const int k_x = kv_xor<D>(lr), kr_x = kr_xor(lr);
+    const uint32_t koff0 = kv_row_off<D>(lr) + 16 * (hh ^ k_x);
+    const uint32_t koff1 = kv_row_off<D>(lr) + 16 * ((2 + hh) ^ k_x);
+    const uint32_t kroff0 = C::KR_OFF + kr_row_off(lr) + 16 * (hh ^ kr_x);
+    const uint32_t kroff1 = C::KR_OFF + kr_row_off(lr) + 16 * ((2 + hh) ^ kr_x);
+    // PV operand (transposing read): issuing lane feeds row 16m + 8u + r0 of
+    // dim block c at 64c + toff[m][u].
+    const int tG = lane >> 4, te = (lane >> 2) & 3, tqd = lane & 3;
+    const int tr_row0 = 4 * (tG >> 1) + te;
+    const int tr_chunk = 2 * (tG & 1) + (tqd >> 1);
+    const int vbase = TIED ? 0 : C::KT_BYTES;
+    int toff[2][2];
 #pragma unroll
-  for (int c = 0; c < C::NC; ++c) {
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      u32x2 w;
-      w[0] = pack_bf2(oacc[c][4 * gq + 0] * inv, oacc[c][4 * gq + 1] * inv);
-      w[1] = pack_bf2(oacc[c][4 * gq + 2] * inv, oacc[c][4 * gq + 3] * inv);
-      *(u32x2*)(orow + 32 * c + 8 * gq + 4 * hh) = w;
+      for (int u = 0; u < 2; ++u) {
+        const int R = 16 * m + 8 * u + tr_row0;
+        toff[m][u] = vbase + kv_row_off<D>(R) + (tqd & 1) * 8 + 16 * (tr_chunk ^ kv_xor<D>(R));
+      }
+
+    auto lds_ptr = [&](int so) { return (const G4_LDS char*)smem + so; };
+    // K fragment of k-step t of the tile in stage `so` (K=V: rotated k-steps
+    // read the Krot slice, chunk 2u + hh with u = t (t < 4) or t - 12).
+    auto kread = [&](int so, int t) -> bf16x8 {
+      if (TIED && rot_step(t)) {
+        const int u = t < 4 ? t : t - 12;
+        return lds_read_b128(lds_ptr(so) + ((u & 1) ? kroff1 : kroff0) + 64 * (u >> 1));
+      }
+      return lds_read_b128(lds_ptr(so) + ((t & 1) ? koff1 : koff0) + 64 * (t >> 1));
+    };
+
+    // Logit of key slot r in the log2 domain is s[r] * c[r]: c = the key's
+    // inverse RMS times scale*log2(e) (K=V, from the tile) or scale*log2(e).
+    const float cs = a.scale_log2;
+    auto key_mul = [&](int so, float (&c)[16]) {
+      if (TIED) {
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const f32x4 v = *(const G4_LDS f32x4*)(lds_ptr(so) + C::R_OFF + (8 * gq + 4 * hh) * 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) c[4 * gq + i] = v[i];
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) c[r] = cs;
+      }
+    };
+    // Does tile kt need element masks (some key not visible from some row)?
+    auto edge_tile = [&](int kt) {
+      const int key0 = kt * kBN;
+      return !((key0 + kBN - 1 <= tq0) && (a.window == 0 || key0 >= tq1 - a.window + 1));
+    };
+    // Key slot r of tile kt is visible iff 0 <= d < w_eff with d = tq - key:
+    // one unsigned compare (a global layer takes w_eff = 2^31 - 1).
+    const uint32_t w_eff = a.window ? (uint32_t)a.window : 0x7fffffffu;
+    auto visible = [&](int kt, int r) {
+      const uint32_t d = (uint32_t)(tq - 4 * hh - kt * kBN) - (uint32_t)(8 * (r >> 2) + (r & 3));
+      return d < w_eff;
+    };
+    // Maximum logit of this lane's 16 slots of tile kt (-inf if none visible).
+    auto tile_max = [&](const f32x16& s, const float (&c)[16], int kt) {
+      const bool edge = edge_tile(kt);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float x = s[r] * c[r];
+        mx = fmaxf(mx, ((!edge) | visible(kt, r)) ? x : -INFINITY);
+      }
+      return mx;
+    };
+
+    // S^T(tile in stage so) = K Q^T, K reads kLook ahead of their MFMA.
+    auto qk = [&](int so) -> f32x16 {
+      bf16x8 ka[kLook + 1];
+#pragma unroll
+      for (int t = 0; t < kLook; ++t) ka[t] = kread(so, t);
+      f32x16 s = f32x16{};
+#pragma unroll
+      for (int t = 0; t < C::NT; ++t) {
+        if (t + kLook < C::NT) ka[(t + kLook) % (kLook + 1)] = kread(so, t + kLook);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % (kLook + 1)], qf[t], s, 0, 0, 0);
+      }
+      return s;
+    };
+
+    // Softmax with a fixed per-row reference m_ref (log2 domain): the row's
+    // maximum over its first tile with a visible key; P = exp2(x - m_ref) is
+    // accumulated without ever rescaling O.  Every P is at most the row sum l,
+    // so a row whose l stays <= 2^64 had no overflow risk; a wave with a larger
+    // (or non-finite) l flags its workgroup, which the REDO launch recomputes
+    // with m_ref = the true row maximum (every P <= 1 then).
+    float m_ref = -INFINITY;
+    float l_part[4] = {0.f, 0.f, 0.f, 0.f};  // four partial row sums: no serial add chain
+    // Masked slots of an edge tile: s = mask_s makes s * c = -inf.
+    auto mask_edge = [&](f32x16& s, int kt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = visible(kt, r) ? s[r] : a.mask_s;
+    };
+    auto first_visible = [&](const f32x16& s, const float (&c)[16], int kt) {
+      if (!REDO && __builtin_amdgcn_ballot_w64(m_ref == -INFINITY)) {  // a row meets its first visible key
+        const float rowmx = max_xor32(tile_max(s, c, kt));
+        m_ref = m_ref == -INFINITY ? rowmx : m_ref;
+      }
+    };
+    // The softmax of one score tile as a list of micro-ops, stage by stage so
+    // that no op waits on the one before it: 16 FMA (x = s c - m), 16 EXP2,
+    // 8 pair sums, 8 row-sum adds, (K=V) 16 multiplies by c, 8 bf16 packs.
+    constexpr int kSmOps = TIED ? 72 : 56;
+    struct Sm {
+      float x[16], ps[8];
+      uint32_t w[8];
+    };
+    // Each op's result is pinned (an empty asm that takes it in and out), so
+    // the op stays in its slot instead of sinking towards the result's use.
+    auto sm_op = [&](Sm& st, const f32x16& s, const float (&c)[16], float m_use, int j) {
+      if (j < 16) {
+        st.x[j] = __builtin_fmaf(s[j], c[j], -m_use);
+        pin(st.x[j]);
+      } else if (j < 32) {
+        st.x[j - 16] = __builtin_amdgcn_exp2f(st.x[j - 16]);
+        pin(st.x[j - 16]);
+      } else if (j < 40) {
+        st.ps[j - 32] = st.x[2 * (j - 32)] + st.x[2 * (j - 32) + 1];
+        pin(st.ps[j - 32]);
+      } else if (j < 48) {
+        l_part[(j - 40) & 3] += st.ps[j - 40];
+        pin(l_part[(j - 40) & 3]);
+      } else if (TIED && j < 64) {
+        st.x[j - 48] *= c[j - 48];
+        pin(st.x[j - 48]);
+      } else {
+        const int i = j - (TIED ? 64 : 48);
+        st.w[i] = pack_bf2(st.x[2 * i], st.x[2 * i + 1]);
+        pin(st.w[i]);
+      }
+    };
+    auto sm_out = [&](const Sm& st, bf16x8 (&pb)[2]) {
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        const u32x4 w = {st.w[4 * mm], st.w[4 * mm + 1], st.w[4 * mm + 2], st.w[4 * mm + 3]};
+        pb[mm] = __builtin_bit_cast(bf16x8, w);
+      }
+    };
+    // P^T operands of score tile s (K=V: P times the key factor).
+    auto softmax = [&](const f32x16& s, const float (&c)[16], bf16x8 (&pb)[2]) {
+      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+      Sm st;
+#pragma unroll
+      for (int j = 0; j < kSmOps; ++j) sm_op(st, s, c, m_use, j);
+      sm_out(st, pb);
+    };
+    // S^T of the tile in stage so, with the softmax of s_prev spread over its
+    // MFMAs: each MFMA is followed by its share of the micro-ops, fenced so the
+    // scheduler keeps this order (the ops run while the MFMA does).
+    // With LOADS, the copy of tile ld_kt into stage ld_so rides along, one
+    // piece after every other MFMA.
+    // ka[0 .. kLook-1] hold the first K fragments, read by the caller.
+    auto qk_softmax = [&](int so, bf16x8 (&ka)[kLook + 1], const f32x16& s_prev, const float (&c)[16],
+                          bf16x8 (&pb)[2], auto loads, int ld_so, int ld_kt) -> f32x16 {
+      constexpr bool LOADS = decltype(loads)::value;
+      const TileSrc ts = tile_src<D, TIED>(a, ld_kt, b, g);
+      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+      Sm st;
+      f32x16 s = f32x16{};
+#pragma unroll
+      for (int t = 0; t < C::NT; ++t) {
+        if (t + kLook < C::NT) ka[(t + kLook) % (kLook + 1)] = kread(so, t + kLook);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % (kLook + 1)], qf[t], s, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = kSmOps * t / C::NT; j < kSmOps * (t + 1) / C::NT; ++j) sm_op(st, s_prev, c, m_use, j);
+        if (LOADS && (t & 1) == 0 && (t >> 1) < TilePieces<D, TIED>::N)
+          load_piece<D, TIED>(a, ts, lds0 + ld_so, wave, lane, t >> 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      sm_out(st, pb);
+      return s;
+    };
+
+    f32x16 oacc[C::NC];
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c) oacc[c] = f32x16{};
+    // O^T += V^T P^T over the tile in stage so, transposing reads kLook ahead.
+    auto pv = [&](int so, const bf16x8 (&pb)[2]) {
+      constexpr int NPV = 2 * C::NC;  // (mm, c) pairs
+      auto vread = [&](int i) -> bf16x8 {
+        const int mm = i / C::NC, c = i % C::NC;
+        const i16x4 lo = lds_read_tr16(lds_ptr(so) + toff[mm][0] + 64 * c);
+        const i16x4 hi = lds_read_tr16(lds_ptr(so) + toff[mm][1] + 64 * c);
+        return cat_tr(lo, hi);
+      };
+      bf16x8 va[kLook + 1];
+#pragma unroll
+      for (int i = 0; i < kLook; ++i) va[i] = vread(i);
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) {
+        if (i + kLook < NPV) va[(i + kLook) % (kLook + 1)] = vread(i + kLook);
+        const int mm = i / C::NC, c = i % C::NC;
+        if (c == 0)
+          mfma_acc<true>(oacc[c], va[i % (kLook + 1)], pb[mm]);
+        else
+          mfma_acc<false>(oacc[c], va[i % (kLook + 1)], pb[mm]);
+      }
+    };
+
+    if (REDO) {
+      // first sweep: the true maximum of every row (stages 0 and 1 hold kt_lo
+      // and kt_lo + 1 already; two-stage ring)
+      float m_run = -INFINITY;
+      int so = 0;
+      for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+        wait_vmem_all();
+        __syncthreads();  // tile kt (and kt + 1) landed; every wave is done with tile kt - 1
+        if (kt > kt_lo && kt < kt_hi) load_tile<D, TIED>(a, lds0 + (C::STAGE - so), kt + 1, b, g, wave, lane);
+        float c[16];
+        key_mul(so, c);
+        const f32x16 s = qk(so);
+        m_run = fmaxf(m_run, tile_max(s, c, kt));
+        so = C::STAGE - so;
+      }
+      m_ref = max_xor32(m_run);
+      __syncthreads();  // every wave is done before the stages are reloaded
+      load_tile<D, TIED>(a, lds0, kt_lo, b, g, wave, lane);
+      if (kt_lo < kt_hi) load_tile<D, TIED>(a, lds0 + C::STAGE, kt_lo + 1, b, g, wave, lane);
     }
-  }
-  if (a.lse && hh == 0) {
-    a.lse[((int64_t)b * a.Hq + head) * a.S + tq] =
-        l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
+
+    wait_vmem_all();
+    __syncthreads();
+    // One pipeline step: softmax + PV of tile kt (scores s_cur) and the scores
+    // of tile kt + 1 into s_nxt.  Written out twice per loop trip with the two
+    // score registers swapped, so neither is ever copied.
+    int so_cur = 0, so_nxt = C::STAGE, so_ld = NST == 3 ? 2 * C::STAGE : 0;
+    auto step = [&](int kt, f32x16& s_cur, f32x16& s_nxt) {
+      wait_vmem_all();  // this wave's copies of tile kt+1 have landed
+      __syncthreads();  // all of tile kt+1 is in LDS; every wave is done with tile kt-1
+      // first K fragments of tile kt+1 right away: their latency hides under
+      // the bookkeeping below
+      bf16x8 ka[kLook + 1];
+#pragma unroll
+      for (int t = 0; t < kLook; ++t) ka[t] = kread(so_nxt, t);
+      float c[16];
+      key_mul(so_cur, c);
+      first_visible(s_cur, c, kt);
+      if (edge_tile(kt)) mask_edge(s_cur, kt);
+      bf16x8 pb[2];
+      // three stages: tile kt+2 goes to the stage tile kt-1 left (past the
+      // end, the last tile is copied again into that unused stage)
+      s_nxt = qk_softmax(so_nxt, ka, s_cur, c, pb, std::integral_constant<bool, NST == 3>{}, so_ld, min(kt + 2, kt_hi));
+      __builtin_amdgcn_sched_barrier(0);
+      pv(so_cur, pb);
+      if (NST == 2 && kt + 2 <= kt_hi) {
+        __syncthreads();  // every wave is done with tile kt
+        load_tile<D, TIED>(a, lds0 + so_cur, kt + 2, b, g, wave, lane);
+      }
+      const int t = so_cur;
+      so_cur = so_nxt;
+      if (NST == 3) { so_nxt = so_ld; so_ld = t; } else { so_nxt = t; }
+    };
+    auto last = [&](f32x16& s_cur) {
+      float c[16];
+      key_mul(so_cur, c);
+      first_visible(s_cur, c, kt_hi);
+      if (edge_tile(kt_hi)) mask_edge(s_cur, kt_hi);
+      bf16x8 pb[2];
+      softmax(s_cur, c, pb);
+      pv(so_cur, pb);
+    };
+    f32x16 sa = qk(0), sb;
+    int kt = kt_lo;
+    for (; kt + 1 < kt_hi; kt += 2) {
+      step(kt, sa, sb);
+      step(kt + 1, sb, sa);
+    }
+    if (kt < kt_hi) {
+      step(kt, sa, sb);
+      sa = sb;
+    }
+    last(sa);
+    wait_vmem_all();  // the extra copy of the last tile has landed before the wave ends
+    // the last MFMA results are read below: 18 wait states cover an 8-pass XDL
+    asm volatile("s_nop 15\n\ts_nop 1"
+                 : "+a"(oacc[0]), "+a"(oacc[1]), "+a"(oacc[2]), "+a"(oacc[3]), "+a"(oacc[4]), "+a"(oacc[5]),
+                   "+a"(oacc[6]), "+a"(oacc[7]));
+    if constexpr (C::NC > 8)
+      asm volatile(""
+                   : "+a"(oacc[8 % C::NC]), "+a"(oacc[9 % C::NC]), "+a"(oacc[10 % C::NC]),
+                     "+a"(oacc[11 % C::NC]), "+a"(oacc[12 % C::NC]), "+a"(oacc[13 % C::NC]),
+                     "+a"(oacc[14 % C::NC]), "+a"(oacc[15 % C::NC]));
+
+    // ---- epilogue: flag, normalise, round once to bf16, store
+    const float l_tot = sum_xor32((l_part[0] + l_part[1]) + (l_part[2] + l_part[3]));
+    if (!REDO) {
+      const bool over = valid && !(l_tot <= 0x1p64f);
+      if (lane == 0) wg_flags[wave] = __builtin_amdgcn_ballot_w64(over) != 0;
+    }
+    if (valid) {
+      // K=V: P carried the factor c = r * scale*log2(e) / qmul; omul undoes it.
+      const float inv = l_tot > 0.f ? (TIED ? a.omul : 1.f) / l_tot : 0.f;
+      uint16_t* orow = a.out + b * a.os[0] + (int64_t)tq * a.os[1] + head * a.os[2];
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c) {
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          u32x2 w;
+          w[0] = pack_bf2(oacc[c][4 * gq + 0] * inv, oacc[c][4 * gq + 1] * inv);
+          w[1] = pack_bf2(oacc[c][4 * gq + 2] * inv, oacc[c][4 * gq + 3] * inv);
+          *(u32x2*)(orow + 32 * c + 8 * gq + 4 * hh) = w;
+        }
+      }
+      if (a.lse && hh == 0) {
+        a.lse[((int64_t)b * a.Hq + head) * a.S + tq] =
+            l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
+      }
+    }
+    if (!REDO) return;
+    __syncthreads();  // every wave is done with the LDS before the next tile reuses it
   }
 }
 
@@ -621,197 +639,212 @@ void prefill_d256_kernel(PrefillArgs a) {
   const int lr = lane & 31;
   const int G = a.Hq / a.Hkv;
   const int ntiles = (int)(((int64_t)a.S * G + BM - 1) / BM);
-  int b, g, tile;
-  wg_map(ntiles, a.Hkv, b, g, tile);
-
-  const int64_t F0 = (int64_t)tile * BM;
-  const int64_t Flast = min(F0 + BM - 1, (int64_t)a.S * G - 1);
-  const int tq0 = (int)(F0 / G), tq1 = (int)(Flast / G);
-  const int64_t F = F0 + wave * 32 + lr;
-  const int tq = (int)(F / G);
-  const int head = g * G + (int)(F % G);
-  const bool valid = tq < a.S;
-
-  const int kt_lo = a.window ? max(0, tq0 - a.window + 1) / kBN : 0;
-  const int kt_hi = tq1 / kBN;
-  int* wg_flags = a.flags + (((int64_t)b * a.Hkv + g) * ntiles + tile) * NW;
-  if (REDO) {
-    int any = 0;
+  // Main pass: one workgroup per row tile.  Recompute pass: a small grid of
+  // persistent workgroups walks every row tile and redoes the flagged ones
+  // (most launches find none, and a full grid of early exits costs ~30 us).
+  const int ntotal = ntiles * a.Hkv * a.B;
+  for (int L = REDO ? (int)blockIdx.x : 0;; L += (int)gridDim.x) {
+    int b, g, tile;
+    if (REDO) {
+      if (L >= ntotal) return;
+      tile = L % ntiles;
+      g = (L / ntiles) % a.Hkv;
+      b = L / (ntiles * a.Hkv);
+      const int* fl = a.flags + (((int64_t)b * a.Hkv + g) * ntiles + tile) * NW;
+      int any = 0;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) any |= wg_flags[w];
-    if (any == 0) return;
-  }
-
-  // Copy of key tile kt: each of the NW waves copies 16/NW row pairs of K
-  // and of V (lanes 0..31 row s, lanes 32..63 row s + 16); rows past S
-  // re-read row S-1 (masked).
-  auto load_tile_w = [&](uint32_t stage, int kt) {
-    const TileSrc ts = tile_src<D, false>(a, kt, b, g);
-    const uint32_t rs = (uint32_t)(a.ks[1] * 2);
-#pragma unroll
-    for (int which = 0; which < 2; ++which)
-#pragma unroll
-      for (int i = 0; i < 16 / NW; ++i) {
-        const int s = wave * (16 / NW) + i;
-        const uint32_t r0 = min((uint32_t)s * rs, ts.last_off);
-        const uint32_t r1 = min((uint32_t)(s + 16) * rs, ts.last_off);
-        const uint32_t off = ((lane >> 5) ? r1 : r0) + (uint32_t)((lane & 31) ^ kv_xor<D>(s)) * 16u;
-        g2lds16s(which ? ts.v : ts.k, off, stage + which * C::KT_BYTES + s * kSeg);
-      }
-  };
-  load_tile_w(lds0, kt_lo);
-
-  bf16x8 qf[C::NT];
-  {
-    const uint16_t* qrow = a.q + b * a.qs[0] + (int64_t)min(tq, a.S - 1) * a.qs[1] + head * a.qs[2];
-#pragma unroll
-    for (int t = 0; t < C::NT; ++t) qf[t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * t + 8 * hh));
-  }
-
-  const int k_x = kv_xor<D>(lr);
-  const uint32_t koff0 = kv_row_off<D>(lr) + 16 * (hh ^ k_x);
-  const uint32_t koff1 = kv_row_off<D>(lr) + 16 * ((2 + hh) ^ k_x);
-  const int tG = lane >> 4, te = (lane >> 2) & 3, tqd = lane & 3;
-  const int tr_row0 = 4 * (tG >> 1) + te;
-  const int tr_chunk = 2 * (tG & 1) + (tqd >> 1);
-  int toff[2][2];
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int R = 16 * m + 8 * u + tr_row0;
-      toff[m][u] = C::KT_BYTES + kv_row_off<D>(R) + (tqd & 1) * 8 + 16 * (tr_chunk ^ kv_xor<D>(R));
+      for (int w = 0; w < NW; ++w) any |= fl[w];
+      if (any == 0) continue;  // uniform: every thread reads the same flags
+    } else {
+      wg_map(ntiles, a.Hkv, b, g, tile);
     }
-  auto lds_ptr = [&](int so) { return (const G4_LDS char*)smem + so; };
 
-  const float cs = a.scale_log2;
-  const uint32_t w_eff = a.window ? (uint32_t)a.window : 0x7fffffffu;
-  auto edge_tile = [&](int kt) {
-    const int key0 = kt * kBN;
-    return !((key0 + kBN - 1 <= tq0) && (a.window == 0 || key0 >= tq1 - a.window + 1));
-  };
-  auto visible = [&](int kt, int r) {
-    const uint32_t d = (uint32_t)(tq - 4 * hh - kt * kBN) - (uint32_t)(8 * (r >> 2) + (r & 3));
-    return d < w_eff;
-  };
-  auto tile_max = [&](const f32x16& s, int kt) {
-    const bool edge = edge_tile(kt);
-    float mx = -INFINITY;
+    const int64_t F0 = (int64_t)tile * BM;
+    const int64_t Flast = min(F0 + BM - 1, (int64_t)a.S * G - 1);
+    const int tq0 = (int)(F0 / G), tq1 = (int)(Flast / G);
+    const int64_t F = F0 + wave * 32 + lr;
+    const int tq = (int)(F / G);
+    const int head = g * G + (int)(F % G);
+    const bool valid = tq < a.S;
+
+    const int kt_lo = a.window ? max(0, tq0 - a.window + 1) / kBN : 0;
+    const int kt_hi = tq1 / kBN;
+    int* wg_flags = a.flags + (((int64_t)b * a.Hkv + g) * ntiles + tile) * NW;
+
+    // Copy of key tile kt: each of the NW waves copies 16/NW row pairs of K
+    // and of V (lanes 0..31 row s, lanes 32..63 row s + 16); rows past S
+    // re-read row S-1 (masked).
+    auto load_tile_w = [&](uint32_t stage, int kt) {
+      const TileSrc ts = tile_src<D, false>(a, kt, b, g);
+      const uint32_t rs = (uint32_t)(a.ks[1] * 2);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, ((!edge) | visible(kt, r)) ? s[r] * cs : -INFINITY);
-    return mx;
-  };
-  auto qk = [&](int so) -> f32x16 {
-    bf16x8 ka[L2 + 1];
-    auto kread = [&](int t) {
-      return lds_read_b128(lds_ptr(so) + ((t & 1) ? koff1 : koff0) + 64 * (t >> 1));
+      for (int which = 0; which < 2; ++which)
+#pragma unroll
+        for (int i = 0; i < 16 / NW; ++i) {
+          const int s = wave * (16 / NW) + i;
+          const uint32_t r0 = min((uint32_t)s * rs, ts.last_off);
+          const uint32_t r1 = min((uint32_t)(s + 16) * rs, ts.last_off);
+          const uint32_t off = ((lane >> 5) ? r1 : r0) + (uint32_t)((lane & 31) ^ kv_xor<D>(s)) * 16u;
+          g2lds16s(which ? ts.v : ts.k, off, stage + which * C::KT_BYTES + s * kSeg);
+        }
     };
-#pragma unroll
-    for (int t = 0; t < L2; ++t) ka[t] = kread(t);
-    f32x16 s = f32x16{};
-#pragma unroll
-    for (int t = 0; t < C::NT; ++t) {
-      if (t + L2 < C::NT) ka[(t + L2) % (L2 + 1)] = kread(t + L2);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % (L2 + 1)], qf[t], s, 0, 0, 0);
-    }
-    return s;
-  };
+    load_tile_w(lds0, kt_lo);
 
-  float m_ref = -INFINITY;
-  float l_part[4] = {0.f, 0.f, 0.f, 0.f};
-  if (REDO) {
-    float m_run = -INFINITY;
+    bf16x8 qf[C::NT];
+    {
+      const uint16_t* qrow = a.q + b * a.qs[0] + (int64_t)min(tq, a.S - 1) * a.qs[1] + head * a.qs[2];
+#pragma unroll
+      for (int t = 0; t < C::NT; ++t) qf[t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * t + 8 * hh));
+    }
+
+    const int k_x = kv_xor<D>(lr);
+    const uint32_t koff0 = kv_row_off<D>(lr) + 16 * (hh ^ k_x);
+    const uint32_t koff1 = kv_row_off<D>(lr) + 16 * ((2 + hh) ^ k_x);
+    const int tG = lane >> 4, te = (lane >> 2) & 3, tqd = lane & 3;
+    const int tr_row0 = 4 * (tG >> 1) + te;
+    const int tr_chunk = 2 * (tG & 1) + (tqd >> 1);
+    int toff[2][2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int R = 16 * m + 8 * u + tr_row0;
+        toff[m][u] = C::KT_BYTES + kv_row_off<D>(R) + (tqd & 1) * 8 + 16 * (tr_chunk ^ kv_xor<D>(R));
+      }
+    auto lds_ptr = [&](int so) { return (const G4_LDS char*)smem + so; };
+
+    const float cs = a.scale_log2;
+    const uint32_t w_eff = a.window ? (uint32_t)a.window : 0x7fffffffu;
+    auto edge_tile = [&](int kt) {
+      const int key0 = kt * kBN;
+      return !((key0 + kBN - 1 <= tq0) && (a.window == 0 || key0 >= tq1 - a.window + 1));
+    };
+    auto visible = [&](int kt, int r) {
+      const uint32_t d = (uint32_t)(tq - 4 * hh - kt * kBN) - (uint32_t)(8 * (r >> 2) + (r & 3));
+      return d < w_eff;
+    };
+    auto tile_max = [&](const f32x16& s, int kt) {
+      const bool edge = edge_tile(kt);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, ((!edge) | visible(kt, r)) ? s[r] * cs : -INFINITY);
+      return mx;
+    };
+    auto qk = [&](int so) -> f32x16 {
+      bf16x8 ka[L2 + 1];
+      auto kread = [&](int t) {
+        return lds_read_b128(lds_ptr(so) + ((t & 1) ? koff1 : koff0) + 64 * (t >> 1));
+      };
+#pragma unroll
+      for (int t = 0; t < L2; ++t) ka[t] = kread(t);
+      f32x16 s = f32x16{};
+#pragma unroll
+      for (int t = 0; t < C::NT; ++t) {
+        if (t + L2 < C::NT) ka[(t + L2) % (L2 + 1)] = kread(t + L2);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % (L2 + 1)], qf[t], s, 0, 0, 0);
+      }
+      return s;
+    };
+
+    float m_ref = -INFINITY;
+    float l_part[4] = {0.f, 0.f, 0.f, 0.f};
+    if (REDO) {
+      float m_run = -INFINITY;
+      int so = 0;
+      for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+        wait_vmem_all();
+        __syncthreads();
+        if (kt < kt_hi) load_tile_w(lds0 + (C::STAGE - so), kt + 1);
+        m_run = fmaxf(m_run, tile_max(qk(so), kt));
+        so = C::STAGE - so;
+      }
+      m_ref = max_xor32(m_run);
+      __syncthreads();
+      load_tile_w(lds0, kt_lo);
+    }
+
+    f32x16 oacc[C::NC];
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c) oacc[c] = f32x16{};
     int so = 0;
     for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-      wait_vmem_all();
-      __syncthreads();
+      wait_vmem_all();  // this wave's copies of tile kt have landed
+      __syncthreads();  // all of tile kt is in LDS; every wave is done with tile kt-1
       if (kt < kt_hi) load_tile_w(lds0 + (C::STAGE - so), kt + 1);
-      m_run = fmaxf(m_run, tile_max(qk(so), kt));
+      f32x16 s = qk(so);
+      if (!REDO && __builtin_amdgcn_ballot_w64(m_ref == -INFINITY)) {
+        const float rowmx = max_xor32(tile_max(s, kt));
+        m_ref = m_ref == -INFINITY ? rowmx : m_ref;
+      }
+      if (edge_tile(kt)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = visible(kt, r) ? s[r] : a.mask_s;
+      }
+      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+      bf16x8 pb[2];
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        u32x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r0 = 8 * mm + 2 * i;
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r0], cs, -m_use));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r0 + 1], cs, -m_use));
+          l_part[i] += p0 + p1;
+          w[i] = pack_bf2(p0, p1);
+        }
+        pb[mm] = __builtin_bit_cast(bf16x8, w);
+      }
+      constexpr int NPV = 2 * C::NC;
+      auto vread = [&](int i) -> bf16x8 {
+        const int mm = i / C::NC, cb = i % C::NC;
+        const i16x4 lo = lds_read_tr16(lds_ptr(so) + toff[mm][0] + 64 * cb);
+        const i16x4 hi = lds_read_tr16(lds_ptr(so) + toff[mm][1] + 64 * cb);
+        return cat_tr(lo, hi);
+      };
+      bf16x8 va[L2 + 1];
+#pragma unroll
+      for (int i = 0; i < L2; ++i) va[i] = vread(i);
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) {
+        if (i + L2 < NPV) va[(i + L2) % (L2 + 1)] = vread(i + L2);
+        const int mm = i / C::NC, cb = i % C::NC;
+        if (cb == 0)
+          mfma_acc<true>(oacc[cb], va[i % (L2 + 1)], pb[mm]);
+        else
+          mfma_acc<false>(oacc[cb], va[i % (L2 + 1)], pb[mm]);
+      }
       so = C::STAGE - so;
     }
-    m_ref = max_xor32(m_run);
-    __syncthreads();
-    load_tile_w(lds0, kt_lo);
-  }
+    asm volatile("s_nop 15\n\ts_nop 1"
+                 : "+a"(oacc[0]), "+a"(oacc[1]), "+a"(oacc[2]), "+a"(oacc[3]), "+a"(oacc[4]), "+a"(oacc[5]),
+                   "+a"(oacc[6]), "+a"(oacc[7]));
 
-  f32x16 oacc[C::NC];
-#pragma unroll
-  for (int c = 0; c < C::NC; ++c) oacc[c] = f32x16{};
-  int so = 0;
-  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-    wait_vmem_all();  // this wave's copies of tile kt have landed
-    __syncthreads();  // all of tile kt is in LDS; every wave is done with tile kt-1
-    if (kt < kt_hi) load_tile_w(lds0 + (C::STAGE - so), kt + 1);
-    f32x16 s = qk(so);
-    if (!REDO && __builtin_amdgcn_ballot_w64(m_ref == -INFINITY)) {
-      const float rowmx = max_xor32(tile_max(s, kt));
-      m_ref = m_ref == -INFINITY ? rowmx : m_ref;
+    const float l_tot = sum_xor32((l_part[0] + l_part[1]) + (l_part[2] + l_part[3]));
+    if (!REDO) {
+      const bool over = valid && !(l_tot <= 0x1p64f);
+      if (lane == 0) wg_flags[wave] = __builtin_amdgcn_ballot_w64(over) != 0;
     }
-    if (edge_tile(kt)) {
+    if (valid) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      uint16_t* orow = a.out + b * a.os[0] + (int64_t)tq * a.os[1] + head * a.os[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = visible(kt, r) ? s[r] : a.mask_s;
-    }
-    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-    bf16x8 pb[2];
+      for (int c = 0; c < C::NC; ++c) {
 #pragma unroll
-    for (int mm = 0; mm < 2; ++mm) {
-      u32x4 w;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r0 = 8 * mm + 2 * i;
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r0], cs, -m_use));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r0 + 1], cs, -m_use));
-        l_part[i] += p0 + p1;
-        w[i] = pack_bf2(p0, p1);
+        for (int gq = 0; gq < 4; ++gq) {
+          u32x2 w;
+          w[0] = pack_bf2(oacc[c][4 * gq + 0] * inv, oacc[c][4 * gq + 1] * inv);
+          w[1] = pack_bf2(oacc[c][4 * gq + 2] * inv, oacc[c][4 * gq + 3] * inv);
+          *(u32x2*)(orow + 32 * c + 8 * gq + 4 * hh) = w;
+        }
       }
-      pb[mm] = __builtin_bit_cast(bf16x8, w);
+      if (a.lse && hh == 0) {
+        a.lse[((int64_t)b * a.Hq + head) * a.S + tq] =
+            l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
+      }
     }
-    constexpr int NPV = 2 * C::NC;
-    auto vread = [&](int i) -> bf16x8 {
-      const int mm = i / C::NC, cb = i % C::NC;
-      const i16x4 lo = lds_read_tr16(lds_ptr(so) + toff[mm][0] + 64 * cb);
-      const i16x4 hi = lds_read_tr16(lds_ptr(so) + toff[mm][1] + 64 * cb);
-      return cat_tr(lo, hi);
-    };
-    bf16x8 va[L2 + 1];
-#pragma unroll
-    for (int i = 0; i < L2; ++i) va[i] = vread(i);
-#pragma unroll
-    for (int i = 0; i < NPV; ++i) {
-      if (i + L2 < NPV) va[(i + L2) % (L2 + 1)] = vread(i + L2);
-      const int mm = i / C::NC, cb = i % C::NC;
-      if (cb == 0)
-        mfma_acc<true>(oacc[cb], va[i % (L2 + 1)], pb[mm]);
-      else
-        mfma_acc<false>(oacc[cb], va[i % (L2 + 1)], pb[mm]);
-    }
-    so = C::STAGE - so;
-  }
-  asm volatile("s_nop 15\n\ts_nop 1"
-               : "+a"(oacc[0]), "+a"(oacc[1]), "+a"(oacc[2]), "+a"(oacc[3]), "+a"(oacc[4]), "+a"(oacc[5]),
-                 "+a"(oacc[6]), "+a"(oacc[7]));
-
-  const float l_tot = sum_xor32((l_part[0] + l_part[1]) + (l_part[2] + l_part[3]));
-  if (!REDO) {
-    const bool over = valid && !(l_tot <= 0x1p64f);
-    if (lane == 0) wg_flags[wave] = __builtin_amdgcn_ballot_w64(over) != 0;
-  }
-  if (!valid) return;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  uint16_t* orow = a.out + b * a.os[0] + (int64_t)tq * a.os[1] + head * a.os[2];
-#pragma unroll
-  for (int c = 0; c < C::NC; ++c) {
-#pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      u32x2 w;
-      w[0] = pack_bf2(oacc[c][4 * gq + 0] * inv, oacc[c][4 * gq + 1] * inv);
-      w[1] = pack_bf2(oacc[c][4 * gq + 2] * inv, oacc[c][4 * gq + 3] * inv);
-      *(u32x2*)(orow + 32 * c + 8 * gq + 4 * hh) = w;
-    }
-  }
-  if (a.lse && hh == 0) {
-    a.lse[((int64_t)b * a.Hq + head) * a.S + tq] =
-        l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
+    if (!REDO) return;
+    __syncthreads();  // every wave is done with the LDS before the next tile reuses it
   }
 }
 
@@ -824,16 +857,21 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   constexpr int kNW256 = 4;  // waves per workgroup of the D = 256 kernel (8: slower, one workgroup per CU)
   const dim3 grid256((unsigned)(((int64_t)a.S * G + 32 * kNW256 - 1) / (32 * kNW256)), (unsigned)a.Hkv,
                      (unsigned)a.B);
+  // recompute pass: persistent workgroups over every row tile
+  auto redo_grid = [&](const dim3& gr) {
+    const int64_t n = (int64_t)gr.x * gr.y * gr.z;
+    return dim3((unsigned)(n < 1024 ? n : 1024));
+  };
   for (int redo = 0; redo < 2; ++redo) {
     if (a.kv_tied)
       hipLaunchKernelGGL((redo ? prefill_kernel<512, true, true> : prefill_kernel<512, true, false>),
-                         grid, dim3(256), 0, st, a);
+                         redo ? redo_grid(grid) : grid, dim3(256), 0, st, a);
     else if (a.D == 512)
-      hipLaunchKernelGGL((redo ? prefill_kernel<512, false, true> : prefill_kernel<512, false, false>), grid,
-                         dim3(256), 0, st, a);
+      hipLaunchKernelGGL((redo ? prefill_kernel<512, false, true> : prefill_kernel<512, false, false>),
+                         redo ? redo_grid(grid) : grid, dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((redo ? prefill_d256_kernel<kNW256, true> : prefill_d256_kernel<kNW256, false>), grid256,
-                         dim3(64 * kNW256), 0, st, a);
+      hipLaunchKernelGGL((redo ? prefill_d256_kernel<kNW256, true> : prefill_d256_kernel<kNW256, false>),
+                         redo ? redo_grid(grid256) : grid256, dim3(64 * kNW256), 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
