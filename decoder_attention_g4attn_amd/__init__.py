@@ -9,6 +9,7 @@ The functions carry the C names of ``include/g4attn.h``:
 
 * :func:`g4attn_norm_rope` - RMSNorm (plain weight) + full / partial RoPE;
 * :func:`g4attn_prefill`   - causal / sliding-window GQA attention, incl. K=V;
+* :func:`g4attn_prefill_chunk` - the same for a chunk of new positions over caches;
 * :func:`g4attn_decode`    - split-KV single-token decode over a KV cache.
 """
 
@@ -22,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libg4attn.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_LAYOUT, ERR_UNSUPPORTED, ERR_CACHE_OVERFLOW, ERR_WORKSPACE, ERR_HIP = range(8)
 
-EXPORTED = ("g4attn_norm_rope", "g4attn_prefill_workspace_bytes", "g4attn_prefill",
+EXPORTED = ("g4attn_norm_rope", "g4attn_prefill_workspace_bytes", "g4attn_prefill", "g4attn_prefill_chunk",
             "g4attn_decode_workspace_bytes", "g4attn_decode", "g4attn_status_str",
             "g4attn_last_hip_error", "g4attn_version")
 
@@ -84,6 +85,10 @@ def load(path=None):
     lib.g4attn_prefill.restype = ctypes.c_int
     lib.g4attn_prefill.argtypes = [ctypes.POINTER(LayerDesc), _P, _P, _P, _P, _P, _P,
                                    ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.g4attn_prefill_chunk.restype = ctypes.c_int
+    lib.g4attn_prefill_chunk.argtypes = [ctypes.POINTER(LayerDesc), _P, _P, _P, ctypes.c_int32, _P, _P,
+                                         ctypes.c_int32, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P,
+                                         ctypes.c_size_t, _P]
     lib.g4attn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.g4attn_decode_workspace_bytes.argtypes = [ctypes.POINTER(LayerDesc), ctypes.c_int32,
                                                   ctypes.c_int32, ctypes.c_int32]
@@ -175,6 +180,33 @@ def g4attn_prefill(desc, q, k, v, out, w_k=None, lse=None, workspace=None, strea
                             _ptr(lse), B, S, _bsh_strides(q), _bsh_strides(k), _bsh_strides(out),
                             _ptr(workspace), wbytes, _stream(stream))
     _raise(st, "g4attn_prefill")
+    return out
+
+
+def g4attn_prefill_chunk(desc, q, k_cache, v_cache, out, pos0, qlen, max_pos, lse=None, workspace=None,
+                         stream=None):
+    """Chunked prefill over caches; see g4attn_prefill_chunk in g4attn.h.  Returns ``out``.
+
+    ``q``/``out`` [B, S, Hq, D]; ``k_cache``, ``v_cache`` contiguous
+    [B, Hkv, cap, D]; ``pos0``, ``qlen`` int32 device tensors [B].
+    """
+    lib = load()
+    _check_bf16(q, k_cache, v_cache, out)
+    for t in (pos0, qlen):
+        if t.dtype != torch.int32:
+            raise TypeError("pos0 and qlen must be int32")
+    for t in (k_cache, v_cache):
+        if not t.is_contiguous():
+            raise ValueError("caches must be contiguous")
+    B, S = q.shape[0], q.shape[1]
+    need = lib.g4attn_prefill_workspace_bytes(ctypes.byref(desc), B, S)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    st = lib.g4attn_prefill_chunk(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), k_cache.shape[2],
+                                  _ptr(pos0), _ptr(qlen), max_pos, _ptr(out), _ptr(lse), B, S,
+                                  _bsh_strides(q), _bsh_strides(out), _ptr(workspace), wbytes, _stream(stream))
+    _raise(st, "g4attn_prefill_chunk")
     return out
 
 

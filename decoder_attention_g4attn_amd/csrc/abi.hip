@@ -215,6 +215,44 @@ g4attn_status g4attn_prefill(const g4attn_layer_desc* d, const g4attn_bf16* q,
   return hip_status(g4attn::launch_prefill(a, s));
 }
 
+g4attn_status g4attn_prefill_chunk(const g4attn_layer_desc* d, const g4attn_bf16* q,
+                                   const g4attn_bf16* k_cache, const g4attn_bf16* v_cache, int32_t cache_cap,
+                                   const int32_t* pos0, const int32_t* qlen, int32_t max_pos,
+                                   g4attn_bf16* out, float* lse, int32_t B, int32_t S,
+                                   const int64_t q_strides[3], const int64_t o_strides[3], void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  g4attn_status st = desc_check(d);
+  if (st != G4ATTN_OK) return st;
+  if (!q || !k_cache || !v_cache || !pos0 || !qlen || !out || !q_strides || !o_strides) return G4ATTN_ERR_NULL;
+  if (d->k_eq_v) return G4ATTN_ERR_UNSUPPORTED;  // a K=V cache would hold X and its side data
+  if (B < 1 || S < 1 || B > 65535 || cache_cap < 1 || max_pos < 0) return G4ATTN_ERR_SHAPE;
+  if ((int64_t)S * (d->num_q_heads / d->num_kv_heads) > (int64_t)INT32_MAX) return G4ATTN_ERR_SHAPE;
+  if (max_pos >= cache_cap) return G4ATTN_ERR_CACHE_OVERFLOW;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return G4ATTN_ERR_LAYOUT;
+  if (!strides_ok(q_strides) || !strides_ok(o_strides)) return G4ATTN_ERR_LAYOUT;
+  const PrefillWs ws = prefill_ws(d, B, S);
+  if (!workspace || workspace_bytes < ws.total || !aligned16(workspace)) return G4ATTN_ERR_WORKSPACE;
+
+  g4attn::PrefillArgs a{};
+  a.q = q; a.k = k_cache; a.v = v_cache; a.out = out; a.lse = lse;
+  a.pos0 = pos0; a.qlen = qlen;
+  a.B = B; a.S = S; a.Hq = d->num_q_heads; a.Hkv = d->num_kv_heads; a.D = d->head_dim;
+  a.window = d->window; a.kv_tied = 0;
+  a.scale_log2 = d->scale * g4attn::kLog2e;
+  if (a.scale_log2 == 0.f) a.scale_log2 = 0x1p-126f;
+  a.mask_s = a.scale_log2 < 0.f ? INFINITY : -INFINITY;
+  a.qmul = 1.f; a.omul = 1.f;
+  // caches [B, Hkv, cap, D]: batch, key (row) and head strides in elements
+  a.ks[0] = (int64_t)d->num_kv_heads * cache_cap * d->head_dim;
+  a.ks[1] = d->head_dim;
+  a.ks[2] = (int64_t)cache_cap * d->head_dim;
+  for (int i = 0; i < 3; ++i) { a.qs[i] = q_strides[i]; a.os[i] = o_strides[i]; }
+  a.flags = (int*)((char*)workspace + ws.flags);
+  return hip_status(g4attn::launch_prefill(a, (hipStream_t)stream));
+}
+
 // Cache rows a decode reads at most: sliding layers keep the last `window`
 // positions in a ring of that many slots, so min(kv_len, window) of them.
 static int32_t decode_rows(const g4attn_layer_desc* d, int32_t max_kv_len) {

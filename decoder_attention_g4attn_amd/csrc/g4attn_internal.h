@@ -155,6 +155,8 @@ struct PrefillArgs {
   const float* r;           // K=V only: [B, Hkv, S] inverse RMS of each key row times scale_log2
   const uint16_t* krot;     // K=V only: [B, Hkv, S, 128]
   int* flags;               // [B, Hkv, ntiles, 4] per-wave reference-overflow flags
+  const int32_t* pos0;      // NULL, or [B] first query position of each sequence (keys from caches)
+  const int32_t* qlen;      // NULL, or [B] valid query rows of each sequence (the rest is padding)
   uint16_t* out;
   float* lse;
   int B, S, Hq, Hkv, D, window, kv_tied;

@@ -89,12 +89,14 @@ struct TileSrc {
   const char* v;      // V row key0
   const char* krot;   // K=V: Krot row key0
   const float* r;     // K=V: key factors from key0
-  uint32_t last_off;  // byte offset of the last in-range row (S-1) from row key0
+  uint32_t last_off;  // byte offset of the last in-range key row (key_end-1) from row key0
   int last;           // its index
 };
 
+// key_end: one past the last valid key of sequence b (S, or the chunk's end
+// when the keys come from a cache).
 template <int D, bool TIED>
-__device__ __forceinline__ TileSrc tile_src(const PrefillArgs& a, int kt, int b, int g) {
+__device__ __forceinline__ TileSrc tile_src(const PrefillArgs& a, int kt, int b, int g, int key_end) {
   const int key0 = kt * kBN;
   TileSrc t;
   const int64_t e = b * a.ks[0] + g * a.ks[2] + (int64_t)key0 * a.ks[1];
@@ -103,7 +105,7 @@ __device__ __forceinline__ TileSrc tile_src(const PrefillArgs& a, int kt, int b,
   const int64_t row0 = ((int64_t)b * a.Hkv + g) * a.S + key0;
   t.krot = TIED ? (const char*)(a.krot + row0 * 128) : nullptr;
   t.r = TIED ? a.r + row0 : nullptr;
-  t.last = a.S - 1 - key0;
+  t.last = key_end - 1 - key0;
   t.last_off = (uint32_t)t.last * (uint32_t)(a.ks[1] * 2);
   return t;
 }
@@ -150,8 +152,8 @@ __device__ __forceinline__ void load_piece(const PrefillArgs& a, const TileSrc& 
 
 template <int D, bool TIED>
 __device__ __forceinline__ void load_tile(const PrefillArgs& a, uint32_t stage, int kt, int b, int g,
-                                          int wave, int lane) {
-  const TileSrc ts = tile_src<D, TIED>(a, kt, b, g);
+                                          int key_end, int wave, int lane) {
+  const TileSrc ts = tile_src<D, TIED>(a, kt, b, g, key_end);
 #pragma unroll
   for (int p = 0; p < TilePieces<D, TIED>::N; ++p) load_piece<D, TIED>(a, ts, stage, wave, lane, p);
 }
@@ -221,7 +223,8 @@ __device__ __forceinline__ void pin(uint32_t& v) { asm volatile("" : "+v"(v)); }
 // in LDS while tile kt+2 is in flight (NST = 3 stages); configurations
 // whose three stages do not fit (D = 512 without K=V) use two stages and
 // load tile kt+2 after PV(kt).
-template <int D, bool TIED, bool REDO>
+// CHUNK: rows continue sequences over caches (pos0 / qlen given).
+template <int D, bool TIED, bool REDO, bool CHUNK>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   typedef Cfg<D, TIED> C;
   constexpr int NST = C::NST;
@@ -253,23 +256,35 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       wg_map(ntiles, a.Hkv, b, g, tile);
     }
 
+    // Rows t < n of this sequence are positions P + t (P = 0, n = S unless
+    // the keys come from a cache: chunked prefill, padded batches).
+    const int P = CHUNK ? a.pos0[b] : 0;
+    const int n = CHUNK ? min(a.qlen[b], a.S) : a.S;
+    const int key_end = P + n;  // keys [0, key_end) exist
     const int64_t F0 = (int64_t)tile * kBM;
     const int64_t Flast = min(F0 + kBM - 1, (int64_t)a.S * G - 1);
-    const int tq0 = (int)(F0 / G), tq1 = (int)(Flast / G);
+    // first and last query positions of the workgroup's valid rows
+    const int tq0 = P + (int)(F0 / G), tq1 = P + (CHUNK ? min((int)(Flast / G), n - 1) : (int)(Flast / G));
     const int64_t F = F0 + wave * 32 + lr;
     const int tq = (int)(F / G);
     const int head = g * G + (int)(F % G);
-    const bool valid = tq < a.S;
+    const bool valid = tq < n;
+    const int pos = P + tq;  // this lane's query position
 
     const int kt_lo = a.window ? max(0, tq0 - a.window + 1) / kBN : 0;
     const int kt_hi = tq1 / kBN;
     int* wg_flags = a.flags + (((int64_t)b * a.Hkv + g) * ntiles + tile) * kWaves;
+    if (CHUNK && tq0 > tq1) {  // only padding rows: nothing to compute (uniform)
+      if (!REDO && threadIdx.x < kWaves) wg_flags[threadIdx.x] = 0;
+      if (!REDO) return;
+      continue;
+    }
 
     // Prefetch the first two tiles, then load this lane's Q^T fragments (rows
     // past S read row S-1; their results are never stored).  K=V: the K-norm
     // weight is folded into the non-rotated dims, times qmul.
-    load_tile<D, TIED>(a, lds0, kt_lo, b, g, wave, lane);
-    if (kt_lo < kt_hi) load_tile<D, TIED>(a, lds0 + C::STAGE, kt_lo + 1, b, g, wave, lane);
+    load_tile<D, TIED>(a, lds0, kt_lo, b, g, key_end, wave, lane);
+    if (kt_lo < kt_hi) load_tile<D, TIED>(a, lds0 + C::STAGE, kt_lo + 1, b, g, key_end, wave, lane);
 
     bf16x8 qf[C::NT];
     {
@@ -347,11 +362,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       const int key0 = kt * kBN;
       return !((key0 + kBN - 1 <= tq0) && (a.window == 0 || key0 >= tq1 - a.window + 1));
     };
-    // Key slot r of tile kt is visible iff 0 <= d < w_eff with d = tq - key:
+    // Key slot r of tile kt is visible iff 0 <= d < w_eff with d = pos - key:
     // one unsigned compare (a global layer takes w_eff = 2^31 - 1).
     const uint32_t w_eff = a.window ? (uint32_t)a.window : 0x7fffffffu;
     auto visible = [&](int kt, int r) {
-      const uint32_t d = (uint32_t)(tq - 4 * hh - kt * kBN) - (uint32_t)(8 * (r >> 2) + (r & 3));
+      const uint32_t d = (uint32_t)(pos - 4 * hh - kt * kBN) - (uint32_t)(8 * (r >> 2) + (r & 3));
       return d < w_eff;
     };
     // Maximum logit of this lane's 16 slots of tile kt (-inf if none visible).
@@ -455,7 +470,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     auto qk_softmax = [&](int so, bf16x8 (&ka)[kLook + 1], const f32x16& s_prev, const float (&c)[16],
                           bf16x8 (&pb)[2], auto loads, int ld_so, int ld_kt) -> f32x16 {
       constexpr bool LOADS = decltype(loads)::value;
-      const TileSrc ts = tile_src<D, TIED>(a, ld_kt, b, g);
+      const TileSrc ts = tile_src<D, TIED>(a, ld_kt, b, g, key_end);
       const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
       Sm st;
       f32x16 s = f32x16{};
@@ -508,7 +523,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       for (int kt = kt_lo; kt <= kt_hi; ++kt) {
         wait_vmem_all();
         __syncthreads();  // tile kt (and kt + 1) landed; every wave is done with tile kt - 1
-        if (kt > kt_lo && kt < kt_hi) load_tile<D, TIED>(a, lds0 + (C::STAGE - so), kt + 1, b, g, wave, lane);
+        if (kt > kt_lo && kt < kt_hi)
+          load_tile<D, TIED>(a, lds0 + (C::STAGE - so), kt + 1, b, g, key_end, wave, lane);
         float c[16];
         key_mul(so, c);
         const f32x16 s = qk(so);
@@ -517,8 +533,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       }
       m_ref = max_xor32(m_run);
       __syncthreads();  // every wave is done before the stages are reloaded
-      load_tile<D, TIED>(a, lds0, kt_lo, b, g, wave, lane);
-      if (kt_lo < kt_hi) load_tile<D, TIED>(a, lds0 + C::STAGE, kt_lo + 1, b, g, wave, lane);
+      load_tile<D, TIED>(a, lds0, kt_lo, b, g, key_end, wave, lane);
+      if (kt_lo < kt_hi) load_tile<D, TIED>(a, lds0 + C::STAGE, kt_lo + 1, b, g, key_end, wave, lane);
     }
 
     wait_vmem_all();
@@ -542,12 +558,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       bf16x8 pb[2];
       // three stages: tile kt+2 goes to the stage tile kt-1 left (past the
       // end, the last tile is copied again into that unused stage)
-      s_nxt = qk_softmax(so_nxt, ka, s_cur, c, pb, std::integral_constant<bool, NST == 3>{}, so_ld, min(kt + 2, kt_hi));
+      s_nxt = qk_softmax(so_nxt, ka, s_cur, c, pb, std::integral_constant<bool, NST == 3>{}, so_ld,
+                         min(kt + 2, kt_hi));
       __builtin_amdgcn_sched_barrier(0);
       pv(so_cur, pb);
       if (NST == 2 && kt + 2 <= kt_hi) {
         __syncthreads();  // every wave is done with tile kt
-        load_tile<D, TIED>(a, lds0 + so_cur, kt + 2, b, g, wave, lane);
+        load_tile<D, TIED>(a, lds0 + so_cur, kt + 2, b, g, key_end, wave, lane);
       }
       const int t = so_cur;
       so_cur = so_nxt;
@@ -624,7 +641,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 // stages (70 KiB); the tile loop is the plain one: copy tile kt+1, S = K Q^T,
 // softmax, O += V^T P^T.  Same layouts, masks, fixed-reference softmax and
 // recompute launch as prefill_kernel.
-template <int NW, bool REDO>
+template <int NW, bool REDO, bool CHUNK>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_d256_kernel(PrefillArgs a) {
   constexpr int D = 256;
@@ -659,23 +676,35 @@ void prefill_d256_kernel(PrefillArgs a) {
       wg_map(ntiles, a.Hkv, b, g, tile);
     }
 
+    // Rows t < n of this sequence are positions P + t (P = 0, n = S unless
+    // the keys come from a cache: chunked prefill, padded batches).
+    const int P = CHUNK ? a.pos0[b] : 0;
+    const int n = CHUNK ? min(a.qlen[b], a.S) : a.S;
+    const int key_end = P + n;  // keys [0, key_end) exist
     const int64_t F0 = (int64_t)tile * BM;
     const int64_t Flast = min(F0 + BM - 1, (int64_t)a.S * G - 1);
-    const int tq0 = (int)(F0 / G), tq1 = (int)(Flast / G);
+    // first and last query positions of the workgroup's valid rows
+    const int tq0 = P + (int)(F0 / G), tq1 = P + (CHUNK ? min((int)(Flast / G), n - 1) : (int)(Flast / G));
     const int64_t F = F0 + wave * 32 + lr;
     const int tq = (int)(F / G);
     const int head = g * G + (int)(F % G);
-    const bool valid = tq < a.S;
+    const bool valid = tq < n;
+    const int pos = P + tq;  // this lane's query position
 
     const int kt_lo = a.window ? max(0, tq0 - a.window + 1) / kBN : 0;
     const int kt_hi = tq1 / kBN;
     int* wg_flags = a.flags + (((int64_t)b * a.Hkv + g) * ntiles + tile) * NW;
+    if (CHUNK && tq0 > tq1) {  // only padding rows: nothing to compute (uniform)
+      if (!REDO && threadIdx.x < NW) wg_flags[threadIdx.x] = 0;
+      if (!REDO) return;
+      continue;
+    }
 
     // Copy of key tile kt: each of the NW waves copies 16/NW row pairs of K
     // and of V (lanes 0..31 row s, lanes 32..63 row s + 16); rows past S
     // re-read row S-1 (masked).
     auto load_tile_w = [&](uint32_t stage, int kt) {
-      const TileSrc ts = tile_src<D, false>(a, kt, b, g);
+      const TileSrc ts = tile_src<D, false>(a, kt, b, g, key_end);
       const uint32_t rs = (uint32_t)(a.ks[1] * 2);
 #pragma unroll
       for (int which = 0; which < 2; ++which)
@@ -720,7 +749,7 @@ void prefill_d256_kernel(PrefillArgs a) {
       return !((key0 + kBN - 1 <= tq0) && (a.window == 0 || key0 >= tq1 - a.window + 1));
     };
     auto visible = [&](int kt, int r) {
-      const uint32_t d = (uint32_t)(tq - 4 * hh - kt * kBN) - (uint32_t)(8 * (r >> 2) + (r & 3));
+      const uint32_t d = (uint32_t)(pos - 4 * hh - kt * kBN) - (uint32_t)(8 * (r >> 2) + (r & 3));
       return d < w_eff;
     };
     auto tile_max = [&](const f32x16& s, int kt) {
@@ -862,16 +891,25 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
     const int64_t n = (int64_t)gr.x * gr.y * gr.z;
     return dim3((unsigned)(n < 1024 ? n : 1024));
   };
+  const bool chunk = a.pos0 != nullptr;  // the ABI passes pos0 and qlen together
   for (int redo = 0; redo < 2; ++redo) {
     if (a.kv_tied)
-      hipLaunchKernelGGL((redo ? prefill_kernel<512, true, true> : prefill_kernel<512, true, false>),
+      hipLaunchKernelGGL((redo ? prefill_kernel<512, true, true, false> : prefill_kernel<512, true, false, false>),
+                         redo ? redo_grid(grid) : grid, dim3(256), 0, st, a);
+    else if (a.D == 512 && chunk)
+      hipLaunchKernelGGL((redo ? prefill_kernel<512, false, true, true> : prefill_kernel<512, false, false, true>),
                          redo ? redo_grid(grid) : grid, dim3(256), 0, st, a);
     else if (a.D == 512)
-      hipLaunchKernelGGL((redo ? prefill_kernel<512, false, true> : prefill_kernel<512, false, false>),
-                         redo ? redo_grid(grid) : grid, dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL((redo ? prefill_d256_kernel<kNW256, true> : prefill_d256_kernel<kNW256, false>),
+      hipLaunchKernelGGL(
+          (redo ? prefill_kernel<512, false, true, false> : prefill_kernel<512, false, false, false>),
+          redo ? redo_grid(grid) : grid, dim3(256), 0, st, a);
+    else if (chunk)
+      hipLaunchKernelGGL((redo ? prefill_d256_kernel<kNW256, true, true> : prefill_d256_kernel<kNW256, false, true>),
                          redo ? redo_grid(grid256) : grid256, dim3(64 * kNW256), 0, st, a);
+    else
+      hipLaunchKernelGGL(
+          (redo ? prefill_d256_kernel<kNW256, true, false> : prefill_d256_kernel<kNW256, false, false>),
+          redo ? redo_grid(grid256) : grid256, dim3(64 * kNW256), 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

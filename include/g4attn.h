@@ -6,6 +6,8 @@
  *                       full or zero-padded partial RoPE;
  *   g4attn_prefill    - causal / sliding-window GQA softmax attention over a
  *                       whole prompt, including the K=V global layer;
+ *   g4attn_prefill_chunk - the same for a chunk of new positions over
+ *                       caches (chunked prefill, padded batches);
  *   g4attn_decode     - one new query token per sequence over a KV cache
  *                       (split-KV plus a log-sum-exp combine).
  *
@@ -159,6 +161,39 @@ g4attn_status g4attn_prefill(const g4attn_layer_desc* desc, const g4attn_bf16* q
                              const int64_t q_strides[3], const int64_t kv_strides[3],
                              const int64_t o_strides[3], void* workspace, size_t workspace_bytes,
                              void* stream);
+
+/*
+ * Chunked prefill over caches (gemma4-pt-claude README, "KV Cache": the
+ * decoder attends over cached keys and values; "Tests": a batched forward
+ * equals the single-sequence one; vinija.ai primer, "Sliding-window
+ * attention"):
+ *
+ *   for b < B, t < qlen[b]:  p = pos0[b] + t
+ *   s_tj   = scale * q[b,t,h] . k_cache[b,g,j],   j <= p  (and p - j < window)
+ *   out[b,t,h] = sum_j softmax_j(s_tj) v_cache[b,g,j],  lse[b,h,t] = log sum_j exp(s_tj)
+ *
+ * A new chunk of S query rows continues sequences whose keys and values
+ * (this chunk's included, e.g. written by g4attn_norm_rope in cache mode at
+ * pos0) sit in linear caches.  Rows t >= qlen[b] are padding: not written.
+ *
+ *   q          [B, S, Hq, D] post-prologue queries, strides q_strides.
+ *   k_cache,   [B, Hkv, cache_cap, D] contiguous post-prologue keys and
+ *   v_cache    values (separate tensors; any window).
+ *   pos0, qlen device int32 [B]: first position and valid rows of each
+ *              sequence (qlen[b] <= S).
+ *   max_pos    host-known bound of every pos0[b] + qlen[b] - 1; >= cache_cap
+ *              is G4ATTN_ERR_CACHE_OVERFLOW.
+ *   out        [B, S, Hq, D] bf16, strides o_strides; lse [B, Hq, S] or NULL.
+ *   workspace  >= g4attn_prefill_workspace_bytes(desc, B, S) bytes.
+ * K=V layers are G4ATTN_ERR_UNSUPPORTED here (their cache would hold the raw
+ * projection and its side data).
+ */
+g4attn_status g4attn_prefill_chunk(const g4attn_layer_desc* desc, const g4attn_bf16* q,
+                                   const g4attn_bf16* k_cache, const g4attn_bf16* v_cache, int32_t cache_cap,
+                                   const int32_t* pos0, const int32_t* qlen, int32_t max_pos,
+                                   g4attn_bf16* out, float* lse, int32_t B, int32_t S,
+                                   const int64_t q_strides[3], const int64_t o_strides[3], void* workspace,
+                                   size_t workspace_bytes, void* stream);
 
 /* Workspace (bytes) that g4attn_decode needs; num_splits as passed to it
  * (a sliding layer's size depends on min(max_kv_len, window) only). */

@@ -61,6 +61,9 @@ Pins (tests/test_oracle_attention.py)
   closed form ``p = L - ((L - s) mod w)``; decode over the ring equals the
   sliding prefill's row ``L`` (the uncached forward) for lengths below, at
   and far past the window.
+* Chunked prefill over caches equals the rows ``pos0 .. pos0 + qlen - 1``
+  of the whole-sequence prefill (the batched/chunked forward equals the
+  single one), padded rows stay empty.
 """
 
 import numpy as np
@@ -267,4 +270,34 @@ def sliding_decode_ring(q, k_ring, v_ring, n, scale, window):
             den = np.sum(e)
             out[b, h] = (e @ vv) / den
             lse[b, h] = mx + np.log(den)
+    return out, lse
+
+
+def prefill_over_cache(q, k_cache, v_cache, pos0, qlen, scale, window):
+    """A chunk of new query rows over caches (chunked prefill, padded batches).
+
+    Row ``t < qlen[b]`` of ``q [B, S, Hq, D]`` is position ``p = pos0[b] + t``
+    and sees cache rows ``j`` of ``k_cache``/``v_cache [B, Hkv, cap, D]`` with
+    :func:`visible` ``(p, j, window)``.  Rows ``t >= qlen[b]`` are padding:
+    zeros and ``lse = -inf``.  Returns ``(out [B, S, Hq, D], lse [B, Hq, S])``.
+    """
+    q = np.asarray(q)
+    B, S, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    out = np.zeros((B, S, Hq, D))
+    lse = np.full((B, Hq, S), -np.inf)
+    for b in range(B):
+        for t in range(int(qlen[b])):
+            p = int(pos0[b]) + t
+            lo = 0 if window == 0 else max(0, p - window + 1)
+            for h in range(Hq):
+                g = _kv_head(h, Hq, Hkv)
+                kk = np.asarray(k_cache[b, g, lo:p + 1, :], np.float64)
+                vv = np.asarray(v_cache[b, g, lo:p + 1, :], np.float64)
+                sc = scale * (kk @ np.asarray(q[b, t, h], np.float64))
+                mx = np.max(sc)
+                e = np.exp(sc - mx)
+                den = np.sum(e)
+                out[b, t, h] = (e @ vv) / den
+                lse[b, h, t] = mx + np.log(den)
     return out, lse

@@ -116,6 +116,26 @@ def test_decode_workspace_sizes():
         assert w == a256(2 * 32 * ns * 512 * 4) + 2 * a256(2 * 32 * ns * 4) + a256(2 * 4 * ns * 4)
 
 
+def test_prefill_chunk_validation():
+    lib = g4.load()
+    qs = I64(16 * 32 * 256, 32 * 256, 256)
+
+    def call(desc=None, q=FAKE, kc=FAKE, vc=FAKE, cap=64, pos0=FAKE, qlen=FAKE, max_pos=40, B=1, S=16,
+             ws=None, wsb=0):
+        desc = desc or _desc(head_dim=256, rotary_dims=256)
+        return lib.g4attn_prefill_chunk(ctypes.byref(desc), q, kc, vc, cap, pos0, qlen, max_pos, FAKE, None, B, S,
+                                        qs, qs, ws, wsb, None)
+
+    assert call(pos0=None) == g4.ERR_NULL
+    assert call(qlen=None) == g4.ERR_NULL
+    assert call(desc=_desc(k_eq_v=True), ws=FAKE, wsb=1 << 30) == g4.ERR_UNSUPPORTED
+    assert call(max_pos=64) == g4.ERR_CACHE_OVERFLOW     # the last position must fit the cache
+    assert call(max_pos=-1) == g4.ERR_SHAPE
+    assert call(S=0) == g4.ERR_SHAPE
+    assert call(q=MISALIGNED) == g4.ERR_LAYOUT
+    assert call() == g4.ERR_WORKSPACE
+
+
 def test_decode_ring_workspace_uses_window_rows():
     """A sliding layer's decode reads at most `window` rows of its ring, however long the sequence."""
     ring = _desc(num_q_heads=32, num_kv_heads=16, head_dim=256, window=1024, rotary_dims=256)

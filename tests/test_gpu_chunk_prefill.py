@@ -1,0 +1,82 @@
+"""Chunked prefill over caches (g4attn_prefill_chunk) against the fp64 oracle through the C ABI:
+position offsets, padded rows, sliding and global layers, both head widths."""
+
+import numpy as np
+import pytest
+import torch
+
+from g4inputs import gen
+from oracle import attention as oat
+from tests._cmp import assert_parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+f64 = gen.to_f64
+SENTINEL = 0x7FC3  # NaN pattern the padding rows must keep
+
+
+def _bf(shape, seed):
+    return gen.normal_bf16(shape, (7, 88, seed, 0), "cpu").to(DEV)
+
+
+def _caches(B, Hkv, cap, D, total, seed):
+    kc = torch.full((B, Hkv, cap, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    vc = torch.full_like(kc, float("nan"))
+    for b, n in enumerate(total):
+        kc[b, :, :n] = _bf((Hkv, n, D), seed + 2 * b)
+        vc[b, :, :n] = _bf((Hkv, n, D), seed + 2 * b + 1)
+    return kc, vc
+
+
+@pytest.mark.parametrize("D,w,Hq,Hkv", [(256, 64, 8, 2), (256, 0, 4, 1), (512, 0, 8, 1), (512, 100, 8, 2)])
+def test_prefill_chunk_vs_oracle(gpu_lib, D, w, Hq, Hkv):
+    g4 = gpu_lib
+    total = [300, 150, 97]          # positions each sequence holds so far, this chunk's included
+    pos0 = [220, 100, 17]
+    qlen = [80, 50, 80]
+    B, S, cap = 3, 80, 320
+    kc, vc = _caches(B, Hkv, cap, D, total, 40)
+    q = _bf((B, S, Hq, D), 50)
+    out = torch.full((B, S, Hq, D), SENTINEL, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=DEV)
+    desc = g4.layer_desc(Hq, Hkv, D, window=w, rotary_dims=D)
+    p0 = torch.tensor(pos0, dtype=torch.int32, device=DEV)
+    ql = torch.tensor(qlen, dtype=torch.int32, device=DEV)
+    g4.g4attn_prefill_chunk(desc, q, kc, vc, out, p0, ql, max(p + n - 1 for p, n in zip(pos0, qlen)), lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = oat.prefill_over_cache(f64(q), f64(kc), f64(vc), pos0, qlen, desc.scale, w)
+    got = np.concatenate([f64(out[b, :qlen[b]]).ravel() for b in range(B)])
+    ref = np.concatenate([ro[b, :qlen[b]].ravel() for b in range(B)])
+    assert_parity(got, ref, f"chunk D={D} w={w} Hq={Hq} Hkv={Hkv}")
+    for b in range(B):
+        np.testing.assert_allclose(lse[b, :, :qlen[b]].cpu().numpy(), rl[b, :, :qlen[b]], rtol=0, atol=2e-3)
+        assert bool((out[b, qlen[b]:].view(torch.int16) == SENTINEL).all()), f"padding rows of sequence {b} written"
+
+
+@pytest.mark.parametrize("D,w", [(256, 48), (512, 0)])
+def test_prefill_chunks_equal_whole_prefill(gpu_lib, D, w):
+    """Three chunks over caches give the rows of one whole-sequence prefill (to the parity bar)."""
+    g4 = gpu_lib
+    B, Sfull, Hq, Hkv, chunk = 2, 300, 8, 2, 100
+    q = _bf((B, Sfull, Hq, D), 60)
+    k = _bf((B, Sfull, Hkv, D), 61)
+    v = _bf((B, Sfull, Hkv, D), 62)
+    desc = g4.layer_desc(Hq, Hkv, D, window=w, rotary_dims=D)
+    whole = torch.empty_like(q)
+    g4.g4attn_prefill(desc, q, k, v, whole)
+    kc = k.permute(0, 2, 1, 3).contiguous()
+    vc = v.permute(0, 2, 1, 3).contiguous()
+    parts = torch.empty_like(q)
+    ql = torch.full((B,), chunk, dtype=torch.int32, device=DEV)
+    for c0 in range(0, Sfull, chunk):
+        p0 = torch.full((B,), c0, dtype=torch.int32, device=DEV)
+        qq = q[:, c0:c0 + chunk].contiguous()
+        oo = torch.empty_like(qq)
+        g4.g4attn_prefill_chunk(desc, qq, kc, vc, oo, p0, ql, c0 + chunk - 1)
+        parts[:, c0:c0 + chunk] = oo
+    torch.cuda.synchronize()
+    assert_parity(f64(parts), f64(whole), f"chunks vs whole D={D} w={w}")
+    # and both against the oracle on the last chunk
+    ro, _ = oat.attention_band(f64(q), f64(k), f64(v), desc.scale, w, rows=np.arange(200, 300))
+    assert_parity(f64(parts[:, 200:]), ro, f"last chunk vs oracle D={D} w={w}")

@@ -215,3 +215,30 @@ def test_planted_ring_slot_off_by_one_fails_forward_pin():
     o, _ = at.sliding_decode_ring(q[:, S - 1], kr, vr, np.array([S]), 1.0 / np.sqrt(D), w)
     ro, _ = at.attention_band(q, k, v, 1.0 / np.sqrt(D), w, rows=np.array([S - 1]))
     assert np.abs(o - ro[:, 0]).max() > 1e-3
+
+
+@pytest.mark.parametrize("w", [0, 5, 16])
+def test_prefill_over_cache_equals_whole_sequence_rows(w):
+    """Chunks of new rows over caches give the whole-sequence prefill's rows; padding stays empty."""
+    B, S, Hq, Hkv, D = 3, 12, 4, 2, 16
+    total = [40, 25, 12]        # positions of each sequence so far (cache rows)
+    pos0 = np.array([28, 20, 0])
+    qlen = np.array([12, 5, 9])  # row t < qlen[b] is position pos0[b] + t
+    scale = 1.0 / np.sqrt(D)
+    cap = 48
+    kc = np.full((B, Hkv, cap, D), np.nan)
+    vc = np.full((B, Hkv, cap, D), np.nan)
+    qc = np.full((B, S, Hq, D), np.nan)
+    refs = []
+    for b in range(B):
+        q, k, v = _qkv(1, total[b], Hq, Hkv, D)
+        kc[b, :, :total[b]] = k[0].transpose(1, 0, 2)
+        vc[b, :, :total[b]] = v[0].transpose(1, 0, 2)
+        qc[b, :qlen[b]] = q[0, pos0[b]:pos0[b] + qlen[b]]
+        rows = np.arange(pos0[b], pos0[b] + qlen[b])
+        refs.append(at.attention_band(q, k, v, scale, w, rows=rows))
+    o, l_ = at.prefill_over_cache(qc, kc, vc, pos0, qlen, scale, w)
+    for b in range(B):
+        np.testing.assert_allclose(o[b, :qlen[b]], refs[b][0][0], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(l_[b, :, :qlen[b]], refs[b][1][0], rtol=0, atol=1e-12)
+        assert np.all(o[b, qlen[b]:] == 0) and np.all(np.isneginf(l_[b, :, qlen[b]:]))
