@@ -67,7 +67,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["sliding", "global", "decode", "sdecode"], default=None,
+    ap.add_argument("--only", choices=["sliding", "global", "decode", "sdecode", "chunk"], default=None,
                     help="time one stage only (profiling aid)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device-to-device copy 3 times (HBM-counter calibration)")
@@ -146,11 +146,30 @@ def build_decode(torch, g4, gen, c):
                 out=torch.empty((c.B, c.Hq, c.D), dtype=torch.bfloat16, device=dev), ws=dws)
 
 
+def build_chunk(torch, g4, gen, c):
+    """Chunked prefill: the last c.S of c.len_hi positions of each sequence; linear K and V
+    caches [B, Hkv, len_hi, D] hold every position (post-prologue rows), the chunk's included."""
+    dev = "cuda"
+    total = c.len_hi
+    kc = gen.normal_bf16((c.B, c.Hkv, total, c.D), gen.seed_key(c.cfg_id, gen.CACHE), dev)
+    vc = gen.normal_bf16((c.B, c.Hkv, total, c.D), gen.seed_key(c.cfg_id, gen.CACHE_V), dev)
+    q_raw = gen.normal_bf16((c.B, c.S, c.Hq, c.D), gen.seed_key(c.cfg_id, gen.Q), dev)
+    wq = gen.norm_weight(c.D, gen.seed_key(c.cfg_id, gen.WQ)).to(dev)
+    desc = g4.layer_desc(c.Hq, c.Hkv, c.D, window=c.window, rotary_dims=c.rotary_dims, rope_theta=c.theta)
+    p0 = total - c.S
+    ws = torch.empty(g4.g4attn_prefill_workspace_bytes(desc, c.B, c.S), dtype=torch.uint8, device=dev)
+    return dict(c=c, desc=desc, kc=kc, vc=vc, q_raw=q_raw, wq=wq, p0=p0, total=total,
+                pos0=torch.full((c.B,), p0, dtype=torch.int32, device=dev),
+                qlen=torch.full((c.B,), c.S, dtype=torch.int32, device=dev),
+                q=torch.empty_like(q_raw), out=torch.empty_like(q_raw), ws=ws)
+
+
 def build_workloads(torch, g4, gen, W):
     st = {"sliding": build_prefill(torch, g4, gen, W["31b_sliding_prefill"]),
           "global": build_prefill(torch, g4, gen, W["31b_global_kv_prefill"]),
           "decode": build_decode(torch, g4, gen, W["31b_global_kv_decode"]),
-          "sdecode": build_decode(torch, g4, gen, W["31b_sliding_decode"])}
+          "sdecode": build_decode(torch, g4, gen, W["31b_sliding_decode"]),
+          "chunk": build_chunk(torch, g4, gen, W["31b_sliding_chunk_prefill"])}
     torch.cuda.synchronize()
     return st
 
@@ -191,6 +210,17 @@ def run_decode_pro(g4, s):
     c = s["c"]
     g4.g4attn_norm_rope(s["q_raw"], s["q"], s["wq"], c.D, c.rotary_dims, c.theta, pos0=s["pos0"],
                         max_pos=s["max_pos"])
+
+
+def run_chunk_pro(g4, s):
+    c = s["c"]
+    g4.g4attn_norm_rope(s["q_raw"], s["q"], s["wq"], c.D, c.rotary_dims, c.theta, pos0=s["pos0"],
+                        max_pos=s["total"] - 1)
+
+
+def run_chunk_attn(g4, s):
+    g4.g4attn_prefill_chunk(s["desc"], s["q"], s["kc"], s["vc"], s["out"], s["pos0"], s["qlen"], s["total"] - 1,
+                            workspace=s["ws"])
 
 
 def run_decode_attn(g4, s):
@@ -266,7 +296,8 @@ def main():
             ("global_prologue", run_global_pro, "global"), ("global_attn", run_global_attn, "global"),
             ("decode_prologue", run_decode_pro, "decode"), ("decode_attn", run_decode_attn, "decode"),
             ("sliding_decode_prologue", run_decode_pro, "sdecode"),
-            ("sliding_decode_attn", run_decode_attn, "sdecode")]
+            ("sliding_decode_attn", run_decode_attn, "sdecode"),
+            ("chunk_prologue", run_chunk_pro, "chunk"), ("chunk_attn", run_chunk_attn, "chunk")]
     if args.only:
         plan = [p for p in plan if p[2] == args.only]
 
@@ -320,6 +351,11 @@ def main():
         res["decode_GBps"] = dec_bytes / avg["decode_attn"] / 1e6
     if "sliding_decode_attn" in avg:
         res["sliding_decode_GBps"] = sdec_bytes / avg["sliding_decode_attn"] / 1e6
+    cc = st["chunk"]["c"]
+    # every chunk row (positions >= window) sees `window` keys
+    fl_chunk = 4.0 * cc.D * sum(min(p + 1, cc.window) for p in range(cc.len_hi - cc.S, cc.len_hi)) * cc.Hq * cc.B
+    if "chunk_attn" in avg:
+        res["chunk_prefill_tflops"] = fl_chunk / avg["chunk_attn"] / 1e9
     prefill_ms = avg.get("sliding_attn", 0.0) + avg.get("global_attn", 0.0)
     prefill_fl = (fl_sliding if "sliding_attn" in avg else 0) + (fl_global if "global_attn" in avg else 0)
     value = prefill_fl / prefill_ms / 1e9 if prefill_ms > 0 else None
@@ -351,6 +387,7 @@ def main():
         "decode_GBps": round(res.get("decode_GBps", 0.0), 1) if "decode_GBps" in res else None,
         "decode_hbm_frac": round(res["decode_GBps"] / PEAK_HBM_GBPS, 4) if "decode_GBps" in res else None,
         "sliding_decode_GBps": round(res["sliding_decode_GBps"], 1) if "sliding_decode_GBps" in res else None,
+        "chunk_prefill_tflops": round(res["chunk_prefill_tflops"], 2) if "chunk_prefill_tflops" in res else None,
         "sliding_prefill_tflops": round(res.get("sliding_prefill_tflops", 0.0), 2) if "sliding_prefill_tflops" in res else None,
         "global_prefill_tflops": round(res.get("global_prefill_tflops", 0.0), 2) if "global_prefill_tflops" in res else None,
         "stage_ms": {k: round(v, 4) for k, v in avg.items()},

@@ -63,6 +63,12 @@ WORKLOADS = {
         "31b_global_kv_decode", 5, "decode", B=32, S=1, Hq=32, Hkv=4, D=512,
         window=0, rotary_dims=128, theta=1e6, k_eq_v=True,
         len_lo=32768, len_hi=131072),
+    # chunked prefill of the 31B sliding layer: the last 4096 of 16384
+    # positions of 2 sequences over linear K/V caches holding all of them
+    "31b_sliding_chunk_prefill": Workload(
+        "31b_sliding_chunk_prefill", 7, "chunk", B=2, S=4096, Hq=32, Hkv=16, D=256,
+        window=1024, rotary_dims=256, theta=1e4, k_eq_v=False,
+        len_lo=16384, len_hi=16384),
     # sliding-layer decode of the same 31B batch over rolling caches
     "31b_sliding_decode": Workload(
         "31b_sliding_decode", 6, "decode", B=32, S=1, Hq=32, Hkv=16, D=256,

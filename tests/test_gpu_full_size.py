@@ -135,3 +135,35 @@ def test_full_size_decode_sampled_heads(gpu_lib, name):
             np.testing.assert_allclose(float(lse[b, h]), m + np.log(e.sum()), rtol=0, atol=LSE_ATOL,
                                        err_msg=f"decode b={b} h={h} lse")
     assert_parity(np.stack(got), np.stack(ref), f"{name} sampled heads")
+
+
+def test_full_size_chunk_prefill_sampled_rows(gpu_lib):
+    """The 31B sliding chunked prefill (last 4096 of 16384 positions over linear caches), as timed."""
+    g4 = gpu_lib
+    c = WORKLOADS["31b_sliding_chunk_prefill"]
+    s = bench.build_chunk(torch, g4, gen, c)
+    lse = torch.empty((c.B, c.Hq, c.S), dtype=torch.float32, device="cuda")
+    bench.run_chunk_pro(g4, s)
+    g4.g4attn_prefill_chunk(s["desc"], s["q"], s["kc"], s["vc"], s["out"], s["pos0"], s["qlen"], s["total"] - 1,
+                            lse=lse, workspace=s["ws"])
+    torch.cuda.synchronize()
+    G = c.Hq // c.Hkv
+    got_all, ref_all = [], []
+    for b in range(c.B):
+        for g in (0, 7, 15):
+            toks = _sample_tokens(c.S, 0, n_rand=6, seed=(c.cfg_id, b, g))
+            heads = [g * G, g * G + G - 1]
+            for t in toks:
+                p = s["p0"] + int(t)
+                qraw = f64(s["q_raw"][b:b + 1, t:t + 1, heads])
+                q = onr.norm_rope(qraw, f64(s["wq"]), np.array([[p]]), c.rotary_dims, c.theta)
+                kk = f64(s["kc"][b, g, p - c.window + 1:p + 1])
+                vv = f64(s["vc"][b, g, p - c.window + 1:p + 1])
+                for hi_, h in enumerate(heads):
+                    sc = c.scale * (kk @ q[0, 0, hi_])
+                    m = sc.max()
+                    e = np.exp(sc - m)
+                    ref_all.append((e @ vv) / e.sum())
+                    got_all.append(f64(s["out"][b, t, h]))
+                    np.testing.assert_allclose(float(lse[b, h, t]), m + np.log(e.sum()), rtol=0, atol=LSE_ATOL)
+    assert_parity(np.stack(got_all), np.stack(ref_all), "31b sliding chunk prefill sampled rows")
