@@ -67,7 +67,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["sliding", "global", "decode", "sdecode", "chunk"], default=None,
+    ap.add_argument("--only", choices=["sliding", "global", "decode", "sdecode", "chunk", "image"], default=None,
                     help="time one stage only (profiling aid)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device-to-device copy 3 times (HBM-counter calibration)")
@@ -101,7 +101,12 @@ def build_prefill(torch, g4, gen, c):
     wk = gen.norm_weight(c.D, gen.seed_key(c.cfg_id, gen.WK)).to(dev)
     desc = g4.layer_desc(c.Hq, c.Hkv, c.D, window=c.window, k_eq_v=c.k_eq_v, rotary_dims=c.rotary_dims,
                          rope_theta=c.theta)
-    s = dict(c=c, desc=desc, q_raw=q_raw, wq=wq, wk=wk, q=torch.empty_like(q_raw), out=torch.empty_like(q_raw))
+    s = dict(c=c, desc=desc, q_raw=q_raw, wq=wq, wk=wk, q=torch.empty_like(q_raw), out=torch.empty_like(q_raw),
+             span_lo=None, span_hi=None)
+    if c.images:
+        lo, hi = gen.image_spans(c.S, c.images)
+        s["span_lo"] = torch.from_numpy(np.tile(lo, (c.B, 1))).to(dev)
+        s["span_hi"] = torch.from_numpy(np.tile(hi, (c.B, 1))).to(dev)
     if c.k_eq_v:
         s["X"] = gen.normal_bf16((c.B, c.S, c.Hkv, c.D), gen.seed_key(c.cfg_id, gen.X), dev)
         s["ws"] = torch.empty(g4.g4attn_prefill_workspace_bytes(desc, c.B, c.S), dtype=torch.uint8, device=dev)
@@ -169,7 +174,8 @@ def build_workloads(torch, g4, gen, W):
           "global": build_prefill(torch, g4, gen, W["31b_global_kv_prefill"]),
           "decode": build_decode(torch, g4, gen, W["31b_global_kv_decode"]),
           "sdecode": build_decode(torch, g4, gen, W["31b_sliding_decode"]),
-          "chunk": build_chunk(torch, g4, gen, W["31b_sliding_chunk_prefill"])}
+          "chunk": build_chunk(torch, g4, gen, W["31b_sliding_chunk_prefill"]),
+          "image": build_prefill(torch, g4, gen, W["31b_sliding_image_prefill"])}
     torch.cuda.synchronize()
     return st
 
@@ -194,7 +200,8 @@ def run_prefill(g4, s, lse=None):
     else:
         g4.g4attn_norm_rope(s["k_raw"], s["k"], s["wk"], c.D, c.rotary_dims, c.theta)
         g4.g4attn_norm_rope(s["v_raw"], s["v"], None, c.D, 0, c.theta)
-        g4.g4attn_prefill(s["desc"], s["q"], s["k"], s["v"], s["out"], lse=lse, workspace=s["ws"])
+        g4.g4attn_prefill(s["desc"], s["q"], s["k"], s["v"], s["out"], lse=lse, workspace=s["ws"],
+                          span_lo=s["span_lo"], span_hi=s["span_hi"])
 
 
 def run_global_pro(g4, s):
@@ -210,6 +217,21 @@ def run_decode_pro(g4, s):
     c = s["c"]
     g4.g4attn_norm_rope(s["q_raw"], s["q"], s["wq"], c.D, c.rotary_dims, c.theta, pos0=s["pos0"],
                         max_pos=s["max_pos"])
+
+
+def run_image_attn(g4, s):
+    g4.g4attn_prefill(s["desc"], s["q"], s["k"], s["v"], s["out"], workspace=s["ws"], span_lo=s["span_lo"],
+                      span_hi=s["span_hi"])
+
+
+def span_pairs(S, window, lo, hi):
+    """Visible (row, key) pairs of one head with bidirectional spans [lo, hi]:
+    the window's (or causal) keys plus each row's span keys outside them."""
+    i = np.arange(S, dtype=np.int64)
+    lo, hi = np.asarray(lo, np.int64), np.asarray(hi, np.int64)
+    base = np.minimum(i + 1, window) if window else i + 1
+    first = i - window + 1 if window else np.zeros_like(i)     # lowest key of the window
+    return int((base + (hi - i) + np.maximum(0, first - lo)).sum())
 
 
 def run_chunk_pro(g4, s):
@@ -297,7 +319,8 @@ def main():
             ("decode_prologue", run_decode_pro, "decode"), ("decode_attn", run_decode_attn, "decode"),
             ("sliding_decode_prologue", run_decode_pro, "sdecode"),
             ("sliding_decode_attn", run_decode_attn, "sdecode"),
-            ("chunk_prologue", run_chunk_pro, "chunk"), ("chunk_attn", run_chunk_attn, "chunk")]
+            ("chunk_prologue", run_chunk_pro, "chunk"), ("chunk_attn", run_chunk_attn, "chunk"),
+            ("image_prologue", run_sliding, "image"), ("image_attn", run_image_attn, "image")]
     if args.only:
         plan = [p for p in plan if p[2] == args.only]
 
@@ -356,6 +379,10 @@ def main():
     fl_chunk = 4.0 * cc.D * sum(min(p + 1, cc.window) for p in range(cc.len_hi - cc.S, cc.len_hi)) * cc.Hq * cc.B
     if "chunk_attn" in avg:
         res["chunk_prefill_tflops"] = fl_chunk / avg["chunk_attn"] / 1e9
+    ci = st["image"]["c"]
+    fl_image = 4.0 * ci.D * span_pairs(ci.S, ci.window, *gen.image_spans(ci.S, ci.images)) * ci.Hq * ci.B
+    if "image_attn" in avg:
+        res["image_prefill_tflops"] = fl_image / avg["image_attn"] / 1e9
     prefill_ms = avg.get("sliding_attn", 0.0) + avg.get("global_attn", 0.0)
     prefill_fl = (fl_sliding if "sliding_attn" in avg else 0) + (fl_global if "global_attn" in avg else 0)
     value = prefill_fl / prefill_ms / 1e9 if prefill_ms > 0 else None
@@ -388,6 +415,7 @@ def main():
         "decode_hbm_frac": round(res["decode_GBps"] / PEAK_HBM_GBPS, 4) if "decode_GBps" in res else None,
         "sliding_decode_GBps": round(res["sliding_decode_GBps"], 1) if "sliding_decode_GBps" in res else None,
         "chunk_prefill_tflops": round(res["chunk_prefill_tflops"], 2) if "chunk_prefill_tflops" in res else None,
+        "image_prefill_tflops": round(res["image_prefill_tflops"], 2) if "image_prefill_tflops" in res else None,
         "sliding_prefill_tflops": round(res.get("sliding_prefill_tflops", 0.0), 2) if "sliding_prefill_tflops" in res else None,
         "global_prefill_tflops": round(res.get("global_prefill_tflops", 0.0), 2) if "global_prefill_tflops" in res else None,
         "stage_ms": {k: round(v, 4) for k, v in avg.items()},

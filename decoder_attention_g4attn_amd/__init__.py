@@ -84,10 +84,10 @@ def load(path=None):
     lib.g4attn_prefill_workspace_bytes.argtypes = [ctypes.POINTER(LayerDesc), ctypes.c_int32, ctypes.c_int32]
     lib.g4attn_prefill.restype = ctypes.c_int
     lib.g4attn_prefill.argtypes = [ctypes.POINTER(LayerDesc), _P, _P, _P, _P, _P, _P,
-                                   ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_size_t, _P]
+                                   ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.g4attn_prefill_chunk.restype = ctypes.c_int
     lib.g4attn_prefill_chunk.argtypes = [ctypes.POINTER(LayerDesc), _P, _P, _P, ctypes.c_int32, _P, _P,
-                                         ctypes.c_int32, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P,
+                                         ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P,
                                          ctypes.c_size_t, _P]
     lib.g4attn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.g4attn_decode_workspace_bytes.argtypes = [ctypes.POINTER(LayerDesc), ctypes.c_int32,
@@ -162,11 +162,20 @@ def g4attn_prefill_workspace_bytes(desc, B, S):
     return load().g4attn_prefill_workspace_bytes(ctypes.byref(desc), B, S)
 
 
-def g4attn_prefill(desc, q, k, v, out, w_k=None, lse=None, workspace=None, stream=None):
+def _spans(span_lo, span_hi):
+    for t in (span_lo, span_hi):
+        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
+            raise TypeError("span bounds must be contiguous int32 [B, S]")
+    return _ptr(span_lo), _ptr(span_hi)
+
+
+def g4attn_prefill(desc, q, k, v, out, w_k=None, lse=None, workspace=None, stream=None, span_lo=None,
+                   span_hi=None):
     """Prefill attention; see g4attn_prefill in g4attn.h.  Returns ``out``.
 
     For a K=V layer (``desc.k_eq_v``) pass the raw tied projection as ``k``,
-    ``v=None`` and the K-norm weight as ``w_k``.  ``workspace`` (a uint8 device
+    ``v=None`` and the K-norm weight as ``w_k``.  ``span_lo``/``span_hi``
+    (int32 [B, S]) add bidirectional spans.  ``workspace`` (a uint8 device
     tensor) is allocated here if not given.
     """
     lib = load()
@@ -176,15 +185,16 @@ def g4attn_prefill(desc, q, k, v, out, w_k=None, lse=None, workspace=None, strea
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lo, hi = _spans(span_lo, span_hi)
     st = lib.g4attn_prefill(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(w_k), _ptr(out),
-                            _ptr(lse), B, S, _bsh_strides(q), _bsh_strides(k), _bsh_strides(out),
+                            _ptr(lse), B, S, _bsh_strides(q), _bsh_strides(k), _bsh_strides(out), lo, hi,
                             _ptr(workspace), wbytes, _stream(stream))
     _raise(st, "g4attn_prefill")
     return out
 
 
 def g4attn_prefill_chunk(desc, q, k_cache, v_cache, out, pos0, qlen, max_pos, lse=None, workspace=None,
-                         stream=None):
+                         stream=None, span_lo=None, span_hi=None):
     """Chunked prefill over caches; see g4attn_prefill_chunk in g4attn.h.  Returns ``out``.
 
     ``q``/``out`` [B, S, Hq, D]; ``k_cache``, ``v_cache`` contiguous
@@ -203,8 +213,9 @@ def g4attn_prefill_chunk(desc, q, k_cache, v_cache, out, pos0, qlen, max_pos, ls
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     wbytes = workspace.numel() * workspace.element_size()
+    lo, hi = _spans(span_lo, span_hi)
     st = lib.g4attn_prefill_chunk(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), k_cache.shape[2],
-                                  _ptr(pos0), _ptr(qlen), max_pos, _ptr(out), _ptr(lse), B, S,
+                                  _ptr(pos0), _ptr(qlen), max_pos, lo, hi, _ptr(out), _ptr(lse), B, S,
                                   _bsh_strides(q), _bsh_strides(out), _ptr(workspace), wbytes, _stream(stream))
     _raise(st, "g4attn_prefill_chunk")
     return out

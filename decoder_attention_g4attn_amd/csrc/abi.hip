@@ -14,7 +14,7 @@ namespace {
 
 thread_local int32_t t_last_hip_error = 0;
 
-constexpr int32_t kVersion = 200;  // 0.2.0: ring caches (sliding-layer decode)
+constexpr int32_t kVersion = 300;  // 0.3.0: chunked prefill, bidirectional spans
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -153,11 +153,13 @@ g4attn_status g4attn_prefill(const g4attn_layer_desc* d, const g4attn_bf16* q,
                              const g4attn_bf16* k, const g4attn_bf16* v, const g4attn_bf16* w_k,
                              g4attn_bf16* out, float* lse, int32_t B, int32_t S,
                              const int64_t q_strides[3], const int64_t kv_strides[3],
-                             const int64_t o_strides[3], void* workspace, size_t workspace_bytes,
-                             void* stream) {
+                             const int64_t o_strides[3], const int32_t* span_lo, const int32_t* span_hi,
+                             void* workspace, size_t workspace_bytes, void* stream) {
   g4attn_status st = desc_check(d);
   if (st != G4ATTN_OK) return st;
   if (!q || !k || !out || !q_strides || !kv_strides || !o_strides) return G4ATTN_ERR_NULL;
+  if (!span_lo != !span_hi) return G4ATTN_ERR_NULL;        // spans come as a pair
+  if (span_lo && d->k_eq_v) return G4ATTN_ERR_UNSUPPORTED;
   if (d->k_eq_v) {
     if (!w_k) return G4ATTN_ERR_NULL;
     if (v) return G4ATTN_ERR_SHAPE;  // K=V takes one tensor
@@ -179,6 +181,7 @@ g4attn_status g4attn_prefill(const g4attn_layer_desc* d, const g4attn_bf16* q,
 
   g4attn::PrefillArgs a{};
   a.q = q; a.k = k; a.v = v; a.w_k = w_k; a.out = out; a.lse = lse;
+  a.span_lo = span_lo; a.span_hi = span_hi;
   a.B = B; a.S = S; a.Hq = d->num_q_heads; a.Hkv = d->num_kv_heads; a.D = d->head_dim;
   a.window = d->window; a.kv_tied = d->k_eq_v;
   a.scale_log2 = d->scale * g4attn::kLog2e;
@@ -218,12 +221,14 @@ g4attn_status g4attn_prefill(const g4attn_layer_desc* d, const g4attn_bf16* q,
 g4attn_status g4attn_prefill_chunk(const g4attn_layer_desc* d, const g4attn_bf16* q,
                                    const g4attn_bf16* k_cache, const g4attn_bf16* v_cache, int32_t cache_cap,
                                    const int32_t* pos0, const int32_t* qlen, int32_t max_pos,
+                                   const int32_t* span_lo, const int32_t* span_hi,
                                    g4attn_bf16* out, float* lse, int32_t B, int32_t S,
                                    const int64_t q_strides[3], const int64_t o_strides[3], void* workspace,
                                    size_t workspace_bytes, void* stream) {
   g4attn_status st = desc_check(d);
   if (st != G4ATTN_OK) return st;
   if (!q || !k_cache || !v_cache || !pos0 || !qlen || !out || !q_strides || !o_strides) return G4ATTN_ERR_NULL;
+  if (!span_lo != !span_hi) return G4ATTN_ERR_NULL;
   if (d->k_eq_v) return G4ATTN_ERR_UNSUPPORTED;  // a K=V cache would hold X and its side data
   if (B < 1 || S < 1 || B > 65535 || cache_cap < 1 || max_pos < 0) return G4ATTN_ERR_SHAPE;
   if ((int64_t)S * (d->num_q_heads / d->num_kv_heads) > (int64_t)INT32_MAX) return G4ATTN_ERR_SHAPE;
@@ -238,6 +243,7 @@ g4attn_status g4attn_prefill_chunk(const g4attn_layer_desc* d, const g4attn_bf16
   g4attn::PrefillArgs a{};
   a.q = q; a.k = k_cache; a.v = v_cache; a.out = out; a.lse = lse;
   a.pos0 = pos0; a.qlen = qlen;
+  a.span_lo = span_lo; a.span_hi = span_hi;
   a.B = B; a.S = S; a.Hq = d->num_q_heads; a.Hkv = d->num_kv_heads; a.D = d->head_dim;
   a.window = d->window; a.kv_tied = 0;
   a.scale_log2 = d->scale * g4attn::kLog2e;

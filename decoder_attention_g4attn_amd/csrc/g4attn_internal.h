@@ -157,6 +157,8 @@ struct PrefillArgs {
   int* flags;               // [B, Hkv, ntiles, 4] per-wave reference-overflow flags
   const int32_t* pos0;      // NULL, or [B] first query position of each sequence (keys from caches)
   const int32_t* qlen;      // NULL, or [B] valid query rows of each sequence (the rest is padding)
+  const int32_t* span_lo;   // NULL, or [B, S] first key of each row's bidirectional span
+  const int32_t* span_hi;   // [B, S] its last key (with span_lo)
   uint16_t* out;
   float* lse;
   int B, S, Hq, Hkv, D, window, kv_tied;

@@ -223,8 +223,10 @@ __device__ __forceinline__ void pin(uint32_t& v) { asm volatile("" : "+v"(v)); }
 // in LDS while tile kt+2 is in flight (NST = 3 stages); configurations
 // whose three stages do not fit (D = 512 without K=V) use two stages and
 // load tile kt+2 after PV(kt).
-// CHUNK: rows continue sequences over caches (pos0 / qlen given).
-template <int D, bool TIED, bool REDO, bool CHUNK>
+// EXT: the extended masks and row layouts: rows that continue sequences
+// over caches (pos0 / qlen) and bidirectional spans (span_lo / span_hi);
+// each is off when its pointer is NULL.
+template <int D, bool TIED, bool REDO, bool EXT>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   typedef Cfg<D, TIED> C;
   constexpr int NST = C::NST;
@@ -258,23 +260,29 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 
     // Rows t < n of this sequence are positions P + t (P = 0, n = S unless
     // the keys come from a cache: chunked prefill, padded batches).
-    const int P = CHUNK ? a.pos0[b] : 0;
-    const int n = CHUNK ? min(a.qlen[b], a.S) : a.S;
+    const int P = EXT && a.pos0 ? a.pos0[b] : 0;
+    const int n = EXT && a.qlen ? min(a.qlen[b], a.S) : a.S;
     const int key_end = P + n;  // keys [0, key_end) exist
     const int64_t F0 = (int64_t)tile * kBM;
     const int64_t Flast = min(F0 + kBM - 1, (int64_t)a.S * G - 1);
     // first and last query positions of the workgroup's valid rows
-    const int tq0 = P + (int)(F0 / G), tq1 = P + (CHUNK ? min((int)(Flast / G), n - 1) : (int)(Flast / G));
+    const int tr0 = (int)(F0 / G), tr1 = EXT ? min((int)(Flast / G), n - 1) : (int)(Flast / G);
+    const int tq0 = P + tr0, tq1 = P + tr1;
     const int64_t F = F0 + wave * 32 + lr;
     const int tq = (int)(F / G);
     const int head = g * G + (int)(F % G);
     const bool valid = tq < n;
     const int pos = P + tq;  // this lane's query position
 
-    const int kt_lo = a.window ? max(0, tq0 - a.window + 1) / kBN : 0;
-    const int kt_hi = tq1 / kBN;
+    // Bidirectional spans: row t also sees keys [span_lo, span_hi] (its own
+    // image span).  The bounds grow with t, so the workgroup's first row has
+    // the lowest and its last valid row the highest.
+    const bool spans = EXT && a.span_lo != nullptr;
+    const int64_t srow = (int64_t)b * a.S;
+    const int kt_lo = min(a.window ? max(0, tq0 - a.window + 1) : 0, spans ? a.span_lo[srow + tr0] : tq0) / kBN;
+    const int kt_hi = min(max(tq1, spans ? a.span_hi[srow + tr1] : tq1), key_end - 1) / kBN;
     int* wg_flags = a.flags + (((int64_t)b * a.Hkv + g) * ntiles + tile) * kWaves;
-    if (CHUNK && tq0 > tq1) {  // only padding rows: nothing to compute (uniform)
+    if (EXT && tq0 > tq1) {  // only padding rows: nothing to compute (uniform)
       if (!REDO && threadIdx.x < kWaves) wg_flags[threadIdx.x] = 0;
       if (!REDO) return;
       continue;
@@ -365,9 +373,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     // Key slot r of tile kt is visible iff 0 <= d < w_eff with d = pos - key:
     // one unsigned compare (a global layer takes w_eff = 2^31 - 1).
     const uint32_t w_eff = a.window ? (uint32_t)a.window : 0x7fffffffu;
-    auto visible = [&](int kt, int r) {
+    // this lane's span: keys [s_lo, s_hi] are visible besides the window
+    const int s_lo = spans ? a.span_lo[srow + min(tq, a.S - 1)] : 0;
+    const int s_hi = spans ? min(a.span_hi[srow + min(tq, a.S - 1)], key_end - 1) : -1;
+    auto visible = [&](int kt, int r) -> bool {
       const uint32_t d = (uint32_t)(pos - 4 * hh - kt * kBN) - (uint32_t)(8 * (r >> 2) + (r & 3));
-      return d < w_eff;
+      if (!spans) return d < w_eff;
+      const int key = pos - (int)d;
+      return (d < w_eff) | ((key >= s_lo) & (key <= s_hi));
     };
     // Maximum logit of this lane's 16 slots of tile kt (-inf if none visible).
     auto tile_max = [&](const f32x16& s, const float (&c)[16], int kt) {
@@ -641,7 +654,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 // stages (70 KiB); the tile loop is the plain one: copy tile kt+1, S = K Q^T,
 // softmax, O += V^T P^T.  Same layouts, masks, fixed-reference softmax and
 // recompute launch as prefill_kernel.
-template <int NW, bool REDO, bool CHUNK>
+template <int NW, bool REDO, bool EXT>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_d256_kernel(PrefillArgs a) {
   constexpr int D = 256;
@@ -678,23 +691,29 @@ void prefill_d256_kernel(PrefillArgs a) {
 
     // Rows t < n of this sequence are positions P + t (P = 0, n = S unless
     // the keys come from a cache: chunked prefill, padded batches).
-    const int P = CHUNK ? a.pos0[b] : 0;
-    const int n = CHUNK ? min(a.qlen[b], a.S) : a.S;
+    const int P = EXT && a.pos0 ? a.pos0[b] : 0;
+    const int n = EXT && a.qlen ? min(a.qlen[b], a.S) : a.S;
     const int key_end = P + n;  // keys [0, key_end) exist
     const int64_t F0 = (int64_t)tile * BM;
     const int64_t Flast = min(F0 + BM - 1, (int64_t)a.S * G - 1);
     // first and last query positions of the workgroup's valid rows
-    const int tq0 = P + (int)(F0 / G), tq1 = P + (CHUNK ? min((int)(Flast / G), n - 1) : (int)(Flast / G));
+    const int tr0 = (int)(F0 / G), tr1 = EXT ? min((int)(Flast / G), n - 1) : (int)(Flast / G);
+    const int tq0 = P + tr0, tq1 = P + tr1;
     const int64_t F = F0 + wave * 32 + lr;
     const int tq = (int)(F / G);
     const int head = g * G + (int)(F % G);
     const bool valid = tq < n;
     const int pos = P + tq;  // this lane's query position
 
-    const int kt_lo = a.window ? max(0, tq0 - a.window + 1) / kBN : 0;
-    const int kt_hi = tq1 / kBN;
+    // Bidirectional spans: row t also sees keys [span_lo, span_hi] (its own
+    // image span).  The bounds grow with t, so the workgroup's first row has
+    // the lowest and its last valid row the highest.
+    const bool spans = EXT && a.span_lo != nullptr;
+    const int64_t srow = (int64_t)b * a.S;
+    const int kt_lo = min(a.window ? max(0, tq0 - a.window + 1) : 0, spans ? a.span_lo[srow + tr0] : tq0) / kBN;
+    const int kt_hi = min(max(tq1, spans ? a.span_hi[srow + tr1] : tq1), key_end - 1) / kBN;
     int* wg_flags = a.flags + (((int64_t)b * a.Hkv + g) * ntiles + tile) * NW;
-    if (CHUNK && tq0 > tq1) {  // only padding rows: nothing to compute (uniform)
+    if (EXT && tq0 > tq1) {  // only padding rows: nothing to compute (uniform)
       if (!REDO && threadIdx.x < NW) wg_flags[threadIdx.x] = 0;
       if (!REDO) return;
       continue;
@@ -748,9 +767,14 @@ void prefill_d256_kernel(PrefillArgs a) {
       const int key0 = kt * kBN;
       return !((key0 + kBN - 1 <= tq0) && (a.window == 0 || key0 >= tq1 - a.window + 1));
     };
-    auto visible = [&](int kt, int r) {
+    // this lane's span: keys [s_lo, s_hi] are visible besides the window
+    const int s_lo = spans ? a.span_lo[srow + min(tq, a.S - 1)] : 0;
+    const int s_hi = spans ? min(a.span_hi[srow + min(tq, a.S - 1)], key_end - 1) : -1;
+    auto visible = [&](int kt, int r) -> bool {
       const uint32_t d = (uint32_t)(pos - 4 * hh - kt * kBN) - (uint32_t)(8 * (r >> 2) + (r & 3));
-      return d < w_eff;
+      if (!spans) return d < w_eff;
+      const int key = pos - (int)d;
+      return (d < w_eff) | ((key >= s_lo) & (key <= s_hi));
     };
     auto tile_max = [&](const f32x16& s, int kt) {
       const bool edge = edge_tile(kt);
@@ -891,7 +915,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
     const int64_t n = (int64_t)gr.x * gr.y * gr.z;
     return dim3((unsigned)(n < 1024 ? n : 1024));
   };
-  const bool chunk = a.pos0 != nullptr;  // the ABI passes pos0 and qlen together
+  const bool chunk = a.pos0 != nullptr || a.span_lo != nullptr;  // the extended variant
   for (int redo = 0; redo < 2; ++redo) {
     if (a.kv_tied)
       hipLaunchKernelGGL((redo ? prefill_kernel<512, true, true, false> : prefill_kernel<512, true, false, false>),

@@ -34,6 +34,7 @@ class Workload:
     k_eq_v: bool
     len_lo: int = 0        # decode: cache lengths drawn from [len_lo, len_hi]
     len_hi: int = 0
+    images: tuple = ()     # prefill: (start, length) image blocks of every sequence
 
     @property
     def scale(self):
@@ -69,6 +70,12 @@ WORKLOADS = {
         "31b_sliding_chunk_prefill", 7, "chunk", B=2, S=4096, Hq=32, Hkv=16, D=256,
         window=1024, rotary_dims=256, theta=1e4, k_eq_v=False,
         len_lo=16384, len_hi=16384),
+    # the 31B sliding prefill with 8 image blocks of 280 tokens per sequence,
+    # attended bidirectionally within each block
+    "31b_sliding_image_prefill": Workload(
+        "31b_sliding_image_prefill", 8, "prefill", B=2, S=16384, Hq=32, Hkv=16, D=256,
+        window=1024, rotary_dims=256, theta=1e4, k_eq_v=False,
+        images=tuple((1000 + 1900 * i, 280) for i in range(8))),
     # sliding-layer decode of the same 31B batch over rolling caches
     "31b_sliding_decode": Workload(
         "31b_sliding_decode", 6, "decode", B=32, S=1, Hq=32, Hkv=16, D=256,

@@ -59,3 +59,15 @@ def decode_lengths(B, lo, hi, key):
 def to_f64(t):
     """Exact widening of a (bf16) torch tensor to a float64 numpy array."""
     return t.detach().to("cpu").to(torch.float32).numpy().astype(np.float64)
+
+
+def image_spans(S, images):
+    """Per-row bidirectional span bounds of one sequence with image blocks at
+    ``(start, length)``: rows of a block get the block's first and last
+    position, text rows their own position.  int32 arrays [S]."""
+    lo = np.arange(S, dtype=np.int32)
+    hi = np.arange(S, dtype=np.int32)
+    for st, n in images:
+        lo[st:st + n] = st
+        hi[st:st + n] = st + n - 1
+    return lo, hi

@@ -147,9 +147,22 @@ size_t g4attn_prefill_workspace_bytes(const g4attn_layer_desc* desc, int32_t B, 
  *              call from one shared tile of X.  head_dim must be 512.
  *   out        [B, S, Hq, D] bf16, strides o_strides.
  *   lse        [B, Hq, S] fp32 (contiguous) or NULL.
+ *   span_lo,   NULL, or device int32 [B, S]: a bidirectional span per row
+ *   span_hi    (the image blocks of multimodal prompts: "Gemma 4" docs, "What
+ *              changed from Gemma 3", NaViT vision tower, and the
+ *              use_bidirectional_vision argument: image tokens attend
+ *              bidirectionally within their block on the sliding-window
+ *              layers; gemma4-pt-claude README, "Tests": the spans survive
+ *              the cached prefill path): row i of sequence b also
+ *              sees keys span_lo[b,i] .. span_hi[b,i], whatever the window
+ *              or causality says.  A text row takes span_lo = span_hi = i.
+ *              Requirements (not checked): span_lo[b,i] <= i <= span_hi[b,i]
+ *              and both non-decreasing in i (contiguous spans); span_hi is
+ *              clamped to S - 1.  Both or neither (else G4ATTN_ERR_NULL);
+ *              not with k_eq_v (G4ATTN_ERR_UNSUPPORTED).
  *   workspace  >= g4attn_prefill_workspace_bytes(desc, B, S) bytes, 16-byte
- *              aligned (per-row softmax maxima and flags; for K=V also the
- *              inverse RMS and rotated slice of each key row).
+ *              aligned (per-wave flags; for K=V also the inverse RMS and
+ *              rotated slice of each key row).
  * Requires S >= 1, B >= 1, and a K/V row stride kv_strides[1] below 2^25
  * elements (G4ATTN_ERR_UNSUPPORTED otherwise: a 32-key tile's row offsets are
  * formed in 32 bits).  Window and causality are applied exactly (integer
@@ -159,8 +172,8 @@ g4attn_status g4attn_prefill(const g4attn_layer_desc* desc, const g4attn_bf16* q
                              const g4attn_bf16* k, const g4attn_bf16* v, const g4attn_bf16* w_k,
                              g4attn_bf16* out, float* lse, int32_t B, int32_t S,
                              const int64_t q_strides[3], const int64_t kv_strides[3],
-                             const int64_t o_strides[3], void* workspace, size_t workspace_bytes,
-                             void* stream);
+                             const int64_t o_strides[3], const int32_t* span_lo, const int32_t* span_hi,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Chunked prefill over caches (gemma4-pt-claude README, "KV Cache": the
@@ -183,6 +196,9 @@ g4attn_status g4attn_prefill(const g4attn_layer_desc* desc, const g4attn_bf16* q
  *              sequence (qlen[b] <= S).
  *   max_pos    host-known bound of every pos0[b] + qlen[b] - 1; >= cache_cap
  *              is G4ATTN_ERR_CACHE_OVERFLOW.
+ *   span_lo,   NULL, or [B, S] bidirectional spans as in g4attn_prefill, in
+ *   span_hi    absolute positions (row t of the chunk is position
+ *              pos0[b] + t); span_hi is clamped to pos0[b] + qlen[b] - 1.
  *   out        [B, S, Hq, D] bf16, strides o_strides; lse [B, Hq, S] or NULL.
  *   workspace  >= g4attn_prefill_workspace_bytes(desc, B, S) bytes.
  * K=V layers are G4ATTN_ERR_UNSUPPORTED here (their cache would hold the raw
@@ -191,6 +207,7 @@ g4attn_status g4attn_prefill(const g4attn_layer_desc* desc, const g4attn_bf16* q
 g4attn_status g4attn_prefill_chunk(const g4attn_layer_desc* desc, const g4attn_bf16* q,
                                    const g4attn_bf16* k_cache, const g4attn_bf16* v_cache, int32_t cache_cap,
                                    const int32_t* pos0, const int32_t* qlen, int32_t max_pos,
+                                   const int32_t* span_lo, const int32_t* span_hi,
                                    g4attn_bf16* out, float* lse, int32_t B, int32_t S,
                                    const int64_t q_strides[3], const int64_t o_strides[3], void* workspace,
                                    size_t workspace_bytes, void* stream);

@@ -24,6 +24,10 @@ Sources
 * Decode over a KV cache: the new query attends over the stored keys and
   values of every earlier token [vinija.ai Gemma 4 primer, "KV cache and
   long-context scaling"; gemma4-pt-claude README, "KV Cache"].
+* Image blocks attend bidirectionally within themselves on the
+  sliding-window layers [Gemma 4 Keras docs, "What changed from Gemma 3",
+  NaViT vision tower, and ``use_bidirectional_vision``]: a row inside an
+  image block also sees every key of its block.
 * Sliding layers keep a window-sized cache [gemma4-pt-claude README, "KV
   Cache": sliding-layer caches hold the window, global ones grow]; decoding
   past the window must agree with the uncached forward pass [same page,
@@ -64,6 +68,10 @@ Pins (tests/test_oracle_attention.py)
 * Chunked prefill over caches equals the rows ``pos0 .. pos0 + qlen - 1``
   of the whole-sequence prefill (the batched/chunked forward equals the
   single one), padded rows stay empty.
+* Span masks: degenerate spans give the plain mask; the masked oracle
+  against torch SDPA with the same boolean mask; one span over a whole
+  global sequence gives unmasked attention; inside a block the mask is all
+  true, outside it the window mask.
 """
 
 import numpy as np
@@ -301,3 +309,46 @@ def prefill_over_cache(q, k_cache, v_cache, pos0, qlen, scale, window):
                 out[b, t, h] = (e @ vv) / den
                 lse[b, h, t] = mx + np.log(den)
     return out, lse
+
+
+def mask_spans(S, window, span_lo, span_hi):
+    """Visibility with bidirectional spans: ``visible(i, j, window)`` or
+    ``span_lo[i] <= j <= span_hi[i]`` (row ``i``'s own image block; a text
+    row has ``span_lo = span_hi = i``)."""
+    i = np.arange(S)[:, None]
+    j = np.arange(S)[None, :]
+    lo = np.asarray(span_lo)[:, None]
+    hi = np.asarray(span_hi)[:, None]
+    return visible(i, j, window) | ((j >= lo) & (j <= hi))
+
+
+def attention_masked(q, k, v, scale, mask):
+    """Brute-force attention under an explicit boolean mask ``[S, S]`` (shared
+    by every batch and head).  Returns ``(out [B, S, Hq, D], lse [B, Hq, S])``."""
+    q = np.asarray(q, np.float64)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    out = np.zeros((B, S, Hq, D))
+    lse = np.full((B, Hq, S), -np.inf)
+    for b in range(B):
+        for h in range(Hq):
+            g = _kv_head(h, Hq, Hkv)
+            s = scale * (q[b, :, h, :] @ np.asarray(k[b, :, g, :], np.float64).T)
+            s = np.where(mask, s, -np.inf)
+            mx = s.max(axis=1, keepdims=True)
+            e = np.exp(s - np.where(np.isfinite(mx), mx, 0.0))
+            den = e.sum(axis=1)
+            out[b, :, h, :] = (e @ np.asarray(v[b, :, g, :], np.float64)) / den[:, None]
+            lse[b, h, :] = mx[:, 0] + np.log(den)
+    return out, lse
+
+
+def span_rows(S, images):
+    """``span_lo``, ``span_hi`` of one sequence whose image blocks are
+    ``(start, length)`` pairs; text rows get ``lo = hi = i``."""
+    lo = np.arange(S)
+    hi = np.arange(S)
+    for st, n in images:
+        lo[st:st + n] = st
+        hi[st:st + n] = st + n - 1
+    return lo, hi

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert g4.g4attn_version() == 200
+    assert g4.g4attn_version() == 300
     for s in range(8):
         assert g4.g4attn_status_str(s)
     assert g4.load().g4attn_last_hip_error() == 0
@@ -47,12 +47,13 @@ def _desc(**kw):
 
 
 def _prefill(desc, q=FAKE, k=FAKE, v=FAKE, wk=None, out=FAKE, B=1, S=16, qs=None, ks=None, os_=None,
-             ws=None, wsb=0):
+             ws=None, wsb=0, span_lo=None, span_hi=None):
     lib = g4.load()
     qs = qs or I64(16 * 32 * 512, 32 * 512, 512)
     ks = ks or I64(16 * 4 * 512, 4 * 512, 512)
     os_ = os_ or I64(16 * 32 * 512, 32 * 512, 512)
-    return lib.g4attn_prefill(ctypes.byref(desc), q, k, v, wk, out, None, B, S, qs, ks, os_, ws, wsb, None)
+    return lib.g4attn_prefill(ctypes.byref(desc), q, k, v, wk, out, None, B, S, qs, ks, os_, span_lo, span_hi,
+                              ws, wsb, None)
 
 
 def test_prefill_validation():
@@ -78,6 +79,9 @@ def test_prefill_validation():
     # flags [1, 4, 1 tile, 4 waves] + r [1, 4, 16] + Krot [1, 4, 16, 128], each 256-byte aligned
     assert need == 256 + 256 + 16 * 4 * 128 * 2
     assert _prefill(kv, wk=FAKE, v=None) == g4.ERR_WORKSPACE
+    # bidirectional spans: both bounds or neither; not on K=V layers
+    assert _prefill(_desc(), span_lo=FAKE) == g4.ERR_NULL
+    assert _prefill(kv, wk=FAKE, v=None, span_lo=FAKE, span_hi=FAKE) == g4.ERR_UNSUPPORTED
     assert _prefill(kv, wk=FAKE, v=None, ws=FAKE, wsb=need - 1) == g4.ERR_WORKSPACE
     assert g4.g4attn_prefill_workspace_bytes(_desc(), 1, 16) == 256
     assert _prefill(_desc()) == g4.ERR_WORKSPACE
@@ -123,8 +127,8 @@ def test_prefill_chunk_validation():
     def call(desc=None, q=FAKE, kc=FAKE, vc=FAKE, cap=64, pos0=FAKE, qlen=FAKE, max_pos=40, B=1, S=16,
              ws=None, wsb=0):
         desc = desc or _desc(head_dim=256, rotary_dims=256)
-        return lib.g4attn_prefill_chunk(ctypes.byref(desc), q, kc, vc, cap, pos0, qlen, max_pos, FAKE, None, B, S,
-                                        qs, qs, ws, wsb, None)
+        return lib.g4attn_prefill_chunk(ctypes.byref(desc), q, kc, vc, cap, pos0, qlen, max_pos, None, None, FAKE,
+                                        None, B, S, qs, qs, ws, wsb, None)
 
     assert call(pos0=None) == g4.ERR_NULL
     assert call(qlen=None) == g4.ERR_NULL

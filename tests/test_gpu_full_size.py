@@ -44,8 +44,9 @@ def _sample_tokens(S, window, n_rand, seed):
 def _prefill_oracle_rows(s, b, g, toks, heads):
     """Oracle out [len(toks), len(heads), D] and lse for batch b, KV group g."""
     c = s["c"]
-    hi = int(toks.max()) + 1
-    lo = 0 if c.window == 0 else max(0, int(toks.min()) - c.window + 1)
+    slo, shi = gen.image_spans(c.S, c.images)
+    hi = int(max(toks.max(), shi[toks].max())) + 1
+    lo = 0 if c.window == 0 else max(0, int(min(toks.min() - c.window + 1, slo[toks].min())))
     pos_k = np.arange(lo, hi)[None, :]
     if c.k_eq_v:
         X = f64(s["X"][b:b + 1, lo:hi, g:g + 1])
@@ -59,8 +60,10 @@ def _prefill_oracle_rows(s, b, g, toks, heads):
         qraw = f64(s["q_raw"][b:b + 1, t:t + 1, heads])                 # [1, 1, H, D]
         q = onr.norm_rope(qraw, f64(s["wq"]), np.array([[t]]), c.rotary_dims, c.theta)
         k0 = 0 if c.window == 0 else max(0, int(t) - c.window + 1)
-        kk = K[0, k0 - lo:t + 1 - lo, 0]                                 # visible keys of row t
-        vv = V[0, k0 - lo:t + 1 - lo, 0]
+        # visible keys of row t: its window (or every earlier key), plus its image block
+        keys = sorted(set(range(k0, int(t) + 1)) | set(range(int(slo[t]), int(shi[t]) + 1)))
+        kk = K[0, np.asarray(keys) - lo, 0]
+        vv = V[0, np.asarray(keys) - lo, 0]
         for hi_, _ in enumerate(heads):
             sc = c.scale * (kk @ q[0, 0, hi_])
             m = sc.max()
@@ -71,7 +74,7 @@ def _prefill_oracle_rows(s, b, g, toks, heads):
 
 
 @pytest.mark.parametrize("name", ["e2b_sliding_prefill", "e2b_global_prefill", "31b_sliding_prefill",
-                                  "31b_global_kv_prefill"])
+                                  "31b_global_kv_prefill", "31b_sliding_image_prefill"])
 def test_full_size_prefill_sampled_rows(gpu_lib, name):
     g4 = gpu_lib
     c = WORKLOADS[name]
@@ -84,6 +87,8 @@ def test_full_size_prefill_sampled_rows(gpu_lib, name):
     for b in range(c.B):
         for g in range(c.Hkv):
             toks = _sample_tokens(c.S, c.window, n_rand=6 if c.Hkv > 4 else 12, seed=(c.cfg_id, b, g))
+            for st, n in c.images[:3]:      # rows at and inside image blocks
+                toks = np.union1d(toks, [st, st + n // 2, st + n - 1])
             # two query heads of the group: the first and the last
             heads = sorted({g * G, g * G + G - 1})
             ro, rl = _prefill_oracle_rows(s, b, g, toks, heads)

@@ -242,3 +242,52 @@ def test_prefill_over_cache_equals_whole_sequence_rows(w):
         np.testing.assert_allclose(o[b, :qlen[b]], refs[b][0][0], rtol=0, atol=1e-12)
         np.testing.assert_allclose(l_[b, :, :qlen[b]], refs[b][1][0], rtol=0, atol=1e-12)
         assert np.all(o[b, qlen[b]:] == 0) and np.all(np.isneginf(l_[b, :, qlen[b]:]))
+
+
+def test_span_mask_structure_and_degenerate_spans():
+    S, w = 40, 8
+    images = [(3, 5), (12, 14), (30, 10)]
+    lo, hi = at.span_rows(S, images)
+    m = at.mask_spans(S, w, lo, hi)
+    plain = at.mask_bruteforce(S, w)
+    for st, n in images:                 # inside a block: everything visible
+        assert m[st:st + n, st:st + n].all()
+    inside = np.zeros((S, S), bool)
+    for st, n in images:
+        inside[st:st + n, st:st + n] = True
+    assert np.array_equal(m & ~inside, plain & ~inside)   # outside: the window mask
+    dlo, dhi = at.span_rows(S, [])
+    assert np.array_equal(at.mask_spans(S, w, dlo, dhi), plain)
+
+
+@pytest.mark.parametrize("w", [0, 6])
+def test_masked_oracle_matches_sdpa_and_band(w):
+    B, S, Hq, Hkv, D = 1, 37, 4, 2, 16
+    q, k, v = _qkv(B, S, Hq, Hkv, D)
+    scale = 1.0 / np.sqrt(D)
+    lo, hi = at.span_rows(S, [(2, 7), (20, 12)])
+    m = at.mask_spans(S, w, lo, hi)
+    o, l_ = at.attention_masked(q, k, v, scale, m)
+    qt = torch.from_numpy(q).permute(0, 2, 1, 3)
+    kt = torch.from_numpy(k).permute(0, 2, 1, 3).repeat_interleave(Hq // Hkv, dim=1)
+    vt = torch.from_numpy(v).permute(0, 2, 1, 3).repeat_interleave(Hq // Hkv, dim=1)
+    ro = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(m), scale=scale)
+    np.testing.assert_allclose(o, ro.permute(0, 2, 1, 3).numpy(), rtol=0, atol=1e-12)
+    # degenerate spans: the band oracle
+    dlo, dhi = at.span_rows(S, [])
+    o2, l2 = at.attention_masked(q, k, v, scale, at.mask_spans(S, w, dlo, dhi))
+    ob, lb = at.attention_band(q, k, v, scale, w)
+    np.testing.assert_allclose(o2, ob, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l2, lb, rtol=0, atol=1e-12)
+
+
+def test_one_span_over_a_global_sequence_is_unmasked_attention():
+    B, S, Hq, Hkv, D = 1, 20, 2, 1, 8
+    q, k, v = _qkv(B, S, Hq, Hkv, D)
+    lo, hi = at.span_rows(S, [(0, S)])
+    o, _ = at.attention_masked(q, k, v, 0.3, at.mask_spans(S, 0, lo, hi))
+    qt = torch.from_numpy(q).permute(0, 2, 1, 3)
+    kt = torch.from_numpy(k).permute(0, 2, 1, 3).repeat_interleave(Hq // Hkv, dim=1)
+    vt = torch.from_numpy(v).permute(0, 2, 1, 3).repeat_interleave(Hq // Hkv, dim=1)
+    ro = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=0.3)
+    np.testing.assert_allclose(o, ro.permute(0, 2, 1, 3).numpy(), rtol=0, atol=1e-12)
