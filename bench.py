@@ -67,7 +67,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["sliding", "global", "decode", "sdecode", "chunk", "image"], default=None,
+    ap.add_argument("--only", choices=["sliding", "global", "decode", "sdecode", "chunk", "image", "rdecode"],
+                    default=None,
                     help="time one stage only (profiling aid)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device-to-device copy 3 times (HBM-counter calibration)")
@@ -151,6 +152,40 @@ def build_decode(torch, g4, gen, c):
                 out=torch.empty((c.B, c.Hq, c.D), dtype=torch.bfloat16, device=dev), ws=dws)
 
 
+def build_decode_raw(torch, g4, gen, c):
+    """K=V decode over the raw-projection cache: X rows 0..L_b of every sequence
+    (drawn like the pre-normed cache) with their inverse RMS and rotated key
+    part appended by g4attn_kv_tied_append (set-up, not timed)."""
+    dev = "cuda"
+    L = gen.decode_lengths(c.B, c.len_lo, c.len_hi, gen.seed_key(c.cfg_id, gen.LENS))
+    n = L.astype(np.int64) + 1
+    cap = c.cache_cap
+    xc = torch.empty((c.B, c.Hkv, cap, c.D), dtype=torch.bfloat16, device=dev)
+    for b in range(c.B):
+        xc[b, :, :n[b]] = gen.normal_bf16((c.Hkv, int(n[b]), c.D), gen.seed_key(c.cfg_id, gen.CACHE, b), dev)
+    rc = torch.empty((c.B, c.Hkv, cap), dtype=torch.float32, device=dev)
+    krc = torch.empty((c.B, c.Hkv, cap, 128), dtype=torch.bfloat16, device=dev)
+    wk = gen.norm_weight(c.D, gen.seed_key(c.cfg_id, gen.WK)).to(dev)
+    for b in range(c.B):   # the cache's own X rows as the projection [1, n_b, Hkv, D] (strided view)
+        xv = xc[b:b + 1, :, :n[b]].permute(0, 2, 1, 3)
+        g4.g4attn_kv_tied_append(xv, wk, xc[b:b + 1], rc[b:b + 1], krc[b:b + 1], c.theta)
+    q_raw = gen.normal_bf16((c.B, 1, c.Hq, c.D), gen.seed_key(c.cfg_id, gen.QDEC), dev)
+    wq = gen.norm_weight(c.D, gen.seed_key(c.cfg_id, gen.WQ)).to(dev)
+    desc = g4.layer_desc(c.Hq, c.Hkv, c.D, window=0, k_eq_v=True, rotary_dims=c.rotary_dims, rope_theta=c.theta)
+    max_len = int(n.max())
+    dws = torch.empty(g4.g4attn_decode_workspace_bytes(desc, c.B, max_len, 0), dtype=torch.uint8, device=dev)
+    return dict(c=c, desc=desc, xc=xc, rc=rc, krc=krc, wk=wk, q_raw=q_raw, wq=wq, L=L, n=n,
+                pos0=torch.from_numpy(L.astype(np.int32)).to(dev), kv_len=torch.from_numpy(n.astype(np.int32)).to(dev),
+                max_len=max_len, max_pos=int(L.max()),
+                q=torch.empty((c.B, 1, c.Hq, c.D), dtype=torch.bfloat16, device=dev),
+                out=torch.empty((c.B, c.Hq, c.D), dtype=torch.bfloat16, device=dev), ws=dws)
+
+
+def run_decode_raw_attn(g4, s):
+    g4.g4attn_decode_tied(s["desc"], s["q"].view(s["q"].shape[0], s["q"].shape[2], s["q"].shape[3]), s["xc"],
+                          s["rc"], s["krc"], s["wk"], s["kv_len"], s["max_len"], s["out"], workspace=s["ws"])
+
+
 def build_chunk(torch, g4, gen, c):
     """Chunked prefill: the last c.S of c.len_hi positions of each sequence; linear K and V
     caches [B, Hkv, len_hi, D] hold every position (post-prologue rows), the chunk's included."""
@@ -175,7 +210,8 @@ def build_workloads(torch, g4, gen, W):
           "decode": build_decode(torch, g4, gen, W["31b_global_kv_decode"]),
           "sdecode": build_decode(torch, g4, gen, W["31b_sliding_decode"]),
           "chunk": build_chunk(torch, g4, gen, W["31b_sliding_chunk_prefill"]),
-          "image": build_prefill(torch, g4, gen, W["31b_sliding_image_prefill"])}
+          "image": build_prefill(torch, g4, gen, W["31b_sliding_image_prefill"]),
+          "rdecode": build_decode_raw(torch, g4, gen, W["31b_global_kv_decode_raw"])}
     torch.cuda.synchronize()
     return st
 
@@ -320,7 +356,8 @@ def main():
             ("sliding_decode_prologue", run_decode_pro, "sdecode"),
             ("sliding_decode_attn", run_decode_attn, "sdecode"),
             ("chunk_prologue", run_chunk_pro, "chunk"), ("chunk_attn", run_chunk_attn, "chunk"),
-            ("image_prologue", run_sliding, "image"), ("image_attn", run_image_attn, "image")]
+            ("image_prologue", run_sliding, "image"), ("image_attn", run_image_attn, "image"),
+            ("raw_decode_prologue", run_decode_pro, "rdecode"), ("raw_decode_attn", run_decode_raw_attn, "rdecode")]
     if args.only:
         plan = [p for p in plan if p[2] == args.only]
 
@@ -383,6 +420,11 @@ def main():
     fl_image = 4.0 * ci.D * span_pairs(ci.S, ci.window, *gen.image_spans(ci.S, ci.images)) * ci.Hq * ci.B
     if "image_attn" in avg:
         res["image_prefill_tflops"] = fl_image / avg["image_attn"] / 1e9
+    rd, crd = st["rdecode"], st["rdecode"]["c"]
+    # X row (2 D bytes) + rotated key part (256 bytes) + inverse RMS (4 bytes) per row per KV head
+    rdec_bytes = float(rd["n"].sum()) * crd.Hkv * (crd.D * 2 + 256 + 4) + 2.0 * crd.B * crd.Hq * crd.D * 2
+    if "raw_decode_attn" in avg:
+        res["raw_kv_decode_GBps"] = rdec_bytes / avg["raw_decode_attn"] / 1e6
     prefill_ms = avg.get("sliding_attn", 0.0) + avg.get("global_attn", 0.0)
     prefill_fl = (fl_sliding if "sliding_attn" in avg else 0) + (fl_global if "global_attn" in avg else 0)
     value = prefill_fl / prefill_ms / 1e9 if prefill_ms > 0 else None
@@ -416,6 +458,7 @@ def main():
         "sliding_decode_GBps": round(res["sliding_decode_GBps"], 1) if "sliding_decode_GBps" in res else None,
         "chunk_prefill_tflops": round(res["chunk_prefill_tflops"], 2) if "chunk_prefill_tflops" in res else None,
         "image_prefill_tflops": round(res["image_prefill_tflops"], 2) if "image_prefill_tflops" in res else None,
+        "raw_kv_decode_GBps": round(res["raw_kv_decode_GBps"], 1) if "raw_kv_decode_GBps" in res else None,
         "sliding_prefill_tflops": round(res.get("sliding_prefill_tflops", 0.0), 2) if "sliding_prefill_tflops" in res else None,
         "global_prefill_tflops": round(res.get("global_prefill_tflops", 0.0), 2) if "global_prefill_tflops" in res else None,
         "stage_ms": {k: round(v, 4) for k, v in avg.items()},

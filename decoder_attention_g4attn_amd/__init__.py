@@ -24,7 +24,8 @@ LIB_PATH = os.path.join(_HERE, "libg4attn.so")
 OK, ERR_NULL, ERR_SHAPE, ERR_LAYOUT, ERR_UNSUPPORTED, ERR_CACHE_OVERFLOW, ERR_WORKSPACE, ERR_HIP = range(8)
 
 EXPORTED = ("g4attn_norm_rope", "g4attn_prefill_workspace_bytes", "g4attn_prefill", "g4attn_prefill_chunk",
-            "g4attn_decode_workspace_bytes", "g4attn_decode", "g4attn_status_str",
+            "g4attn_decode_workspace_bytes", "g4attn_decode", "g4attn_kv_tied_append", "g4attn_decode_tied",
+            "g4attn_status_str",
             "g4attn_last_hip_error", "g4attn_version")
 
 
@@ -96,6 +97,13 @@ def load(path=None):
     lib.g4attn_decode.argtypes = [ctypes.POINTER(LayerDesc), _P, _P, _P, _P, ctypes.c_int32,
                                   ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int32, _P,
                                   ctypes.c_size_t, _P]
+    lib.g4attn_kv_tied_append.restype = ctypes.c_int
+    lib.g4attn_kv_tied_append.argtypes = [_P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_float, ctypes.c_float, _P, _P, ctypes.c_int32, _P, _P, _P,
+                                          ctypes.c_int32, _P]
+    lib.g4attn_decode_tied.restype = ctypes.c_int
+    lib.g4attn_decode_tied.argtypes = [ctypes.POINTER(LayerDesc), _P, _P, _P, _P, _P, _P, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int32, _P, ctypes.c_size_t, _P]
     lib.g4attn_status_str.restype = ctypes.c_char_p
     lib.g4attn_status_str.argtypes = [ctypes.c_int]
     lib.g4attn_last_hip_error.restype = ctypes.c_int32
@@ -252,6 +260,47 @@ def g4attn_decode(desc, q, k_cache, v_cache, kv_len, max_kv_len, out, lse=None, 
                            B, max_kv_len, cap, _ptr(out), _ptr(lse), num_splits, _ptr(workspace),
                            wbytes, _stream(stream))
     _raise(st, "g4attn_decode")
+    return out
+
+
+def g4attn_kv_tied_append(x, w_k, x_cache, r_cache, krot_cache, rope_theta, rms_eps=1e-6, pos0=None,
+                          max_pos=None, rotary_dims=128, stream=None):
+    """Append raw K=V rows X [B, S, Hkv, 512] to a K=V cache; see g4attn_kv_tied_append."""
+    lib = load()
+    _check_bf16(x, w_k, x_cache, krot_cache)
+    if r_cache.dtype != torch.float32:
+        raise TypeError("r_cache is float32")
+    for t in (x_cache, r_cache, krot_cache):
+        if not t.is_contiguous():
+            raise ValueError("caches must be contiguous")
+    B, S, Hkv, _ = x.shape
+    if max_pos is None:
+        max_pos = S - 1 if pos0 is None else int(pos0.max().item()) + S - 1
+    st = lib.g4attn_kv_tied_append(_ptr(x), _ptr(w_k), B, S, Hkv, rotary_dims, rope_theta, rms_eps,
+                                   _bsh_strides(x), _ptr(pos0), max_pos, _ptr(x_cache), _ptr(r_cache),
+                                   _ptr(krot_cache), x_cache.shape[2], _stream(stream))
+    _raise(st, "g4attn_kv_tied_append")
+
+
+def g4attn_decode_tied(desc, q, x_cache, r_cache, krot_cache, w_k, kv_len, max_kv_len, out, lse=None,
+                       num_splits=0, workspace=None, stream=None):
+    """K=V decode over the raw-projection cache; see g4attn_decode_tied in g4attn.h.  Returns ``out``."""
+    lib = load()
+    _check_bf16(q, x_cache, krot_cache, w_k, out)
+    if kv_len.dtype != torch.int32:
+        raise TypeError("kv_len must be int32")
+    for t in (q, x_cache, r_cache, krot_cache, out):
+        if not t.is_contiguous():
+            raise ValueError("decode tensors must be contiguous")
+    B = q.shape[0]
+    need = lib.g4attn_decode_workspace_bytes(ctypes.byref(desc), B, max_kv_len, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    st = lib.g4attn_decode_tied(ctypes.byref(desc), _ptr(q), _ptr(x_cache), _ptr(r_cache), _ptr(krot_cache),
+                                _ptr(w_k), _ptr(kv_len), B, max_kv_len, x_cache.shape[2], _ptr(out), _ptr(lse),
+                                num_splits, _ptr(workspace), wbytes, _stream(stream))
+    _raise(st, "g4attn_decode_tied")
     return out
 
 

@@ -14,7 +14,7 @@ namespace {
 
 thread_local int32_t t_last_hip_error = 0;
 
-constexpr int32_t kVersion = 300;  // 0.3.0: chunked prefill, bidirectional spans
+constexpr int32_t kVersion = 400;  // 0.4.0: K=V decode over the raw-projection cache
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -317,6 +317,73 @@ g4attn_status g4attn_decode(const g4attn_layer_desc* d, const g4attn_bf16* q,
   a.nsplit = (int)ns; a.chunk = (int)c; a.max_len = rows;  // kv_len is clamped to rows in the kernel
   a.scale_log2 = d->scale * g4attn::kLog2e;
   return hip_status(g4attn::launch_decode(a, (hipStream_t)stream));
+}
+
+g4attn_status g4attn_kv_tied_append(const g4attn_bf16* x, const g4attn_bf16* w_k, int32_t B, int32_t S,
+                                    int32_t Hkv, int32_t rotary_dims, float rope_theta, float rms_eps,
+                                    const int64_t x_strides[3], const int32_t* pos0, int32_t max_pos,
+                                    g4attn_bf16* x_cache, float* r_cache, g4attn_bf16* krot_cache,
+                                    int32_t cache_cap, void* stream) {
+  if (!x || !w_k || !x_strides || !x_cache || !r_cache || !krot_cache) return G4ATTN_ERR_NULL;
+  if (B < 1 || S < 1 || Hkv < 1 || B > 65535 || cache_cap < 1) return G4ATTN_ERR_SHAPE;
+  if (rotary_dims != 128) return G4ATTN_ERR_UNSUPPORTED;
+  if (!(rope_theta > 0.f) || !isfinite(rope_theta) || !(rms_eps >= 0.f) || !isfinite(rms_eps))
+    return G4ATTN_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(w_k) || !aligned16(x_cache) || !aligned16(krot_cache) ||
+      (reinterpret_cast<uintptr_t>(r_cache) & 3u))
+    return G4ATTN_ERR_LAYOUT;
+  if (!strides_ok(x_strides)) return G4ATTN_ERR_LAYOUT;
+  if (pos0 && max_pos < S - 1) return G4ATTN_ERR_SHAPE;
+  const int64_t top = pos0 ? (int64_t)max_pos : (int64_t)S - 1;
+  if (top >= cache_cap) return G4ATTN_ERR_CACHE_OVERFLOW;
+  g4attn::KvPrepArgs p{};
+  p.x = x; p.w_k = w_k; p.r = r_cache; p.krot = krot_cache; p.x_out = x_cache;
+  p.pos0 = pos0; p.cap = cache_cap;
+  p.B = B; p.S = S; p.Hkv = Hkv; p.rot = rotary_dims;
+  p.log2_theta = log2((double)rope_theta);
+  p.eps = rms_eps;
+  p.rscale = 1.f;
+  for (int i = 0; i < 3; ++i) p.xs[i] = x_strides[i];
+  return hip_status(g4attn::launch_kv_prep(p, (hipStream_t)stream));
+}
+
+g4attn_status g4attn_decode_tied(const g4attn_layer_desc* d, const g4attn_bf16* q, const g4attn_bf16* x_cache,
+                                 const float* r_cache, const g4attn_bf16* krot_cache, const g4attn_bf16* w_k,
+                                 const int32_t* kv_len, int32_t B, int32_t max_kv_len, int32_t cache_cap,
+                                 g4attn_bf16* out, float* lse, int32_t num_splits, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  g4attn_status st = desc_check(d);
+  if (st != G4ATTN_OK) return st;
+  if (!q || !x_cache || !r_cache || !krot_cache || !w_k || !kv_len || !out) return G4ATTN_ERR_NULL;
+  if (!d->k_eq_v || d->head_dim != 512 || d->rotary_dims != 128 || d->window != 0) return G4ATTN_ERR_UNSUPPORTED;
+  if (d->num_q_heads / d->num_kv_heads > 16) return G4ATTN_ERR_UNSUPPORTED;
+  if (B < 1 || B > 65535 || max_kv_len < 1 || cache_cap < 1 || num_splits < 0) return G4ATTN_ERR_SHAPE;
+  if (max_kv_len > cache_cap) return G4ATTN_ERR_CACHE_OVERFLOW;
+  if (!aligned16(q) || !aligned16(x_cache) || !aligned16(krot_cache) || !aligned16(w_k) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(r_cache) & 3u) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return G4ATTN_ERR_LAYOUT;
+  const int64_t c = decode_chunk(d, B, max_kv_len, num_splits);
+  const int64_t ns = ((int64_t)max_kv_len + c - 1) / c;
+  if (ns > 65535) return G4ATTN_ERR_SHAPE;
+  const size_t need = g4attn_decode_workspace_bytes(d, B, max_kv_len, num_splits);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return G4ATTN_ERR_WORKSPACE;
+
+  const size_t ph = (size_t)B * d->num_q_heads;
+  g4attn::DecodeArgs a{};
+  a.q = q; a.kc = x_cache; a.vc = x_cache; a.kv_len = kv_len; a.out = out; a.lse = lse;
+  a.rc = r_cache; a.krc = krot_cache; a.w_k = w_k;
+  char* wsp = (char*)workspace;
+  a.o_part = (float*)wsp;
+  wsp += align256(ph * ns * d->head_dim * sizeof(float));
+  a.lse_part = (float*)wsp;
+  wsp += align256(ph * ns * sizeof(float));
+  a.dmax = (float*)wsp;
+  wsp += align256(ph * ns * sizeof(float));
+  a.dflags = (int*)wsp;
+  a.B = B; a.Hq = d->num_q_heads; a.Hkv = d->num_kv_heads; a.D = d->head_dim; a.cap = cache_cap;
+  a.nsplit = (int)ns; a.chunk = (int)c; a.max_len = max_kv_len;
+  a.scale_log2 = d->scale * g4attn::kLog2e;
+  return hip_status(g4attn::launch_decode_tied(a, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -240,6 +240,198 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   }
 }
 
+// K=V decode over the raw tied projection (the global layer's own cache
+// format): the cache holds X, the inverse RMS r of each row and the rotated
+// part Krot = RoPE(X w_k) of its key on dims 0..63, 256..319.  With q's
+// K-norm weight folded into its other dims, as in the K=V prefill,
+//   q.k_p = r_p (sum_{d not in R} (q_d w_d) X_pd + sum_{d in R} q_d Krot_pd),
+//   sum_p P_p v_p = sum_p (P_p r_p) X_p,
+// so one LDS tile of X (plus 16 Krot rows and 16 factors) feeds both MFMAs.
+// 1284 bytes per cached row and KV head, read once.  Three waves x two
+// stages (the Krot slice does not fit a fourth wave's ring).
+constexpr int kWavesT = 3;
+constexpr int kTileX = kRows * kSegD;           // 16 X rows
+constexpr int kKrOff = kTileX;                  // 16 Krot rows of 256 B, chunk c of row r at slot c ^ r
+constexpr int kROff = kKrOff + kRows * 256;     // 64 factors (16 used)
+constexpr int kStageT = kROff + 256;
+
+__device__ __forceinline__ constexpr bool rot_step32(int t) { return t < 2 || (t >= 8 && t < 10); }
+
+template <bool REDO>
+__global__ __launch_bounds__(kWavesT * 64) void decode_tied_kernel(DecodeArgs a) {
+  constexpr int D = 512, NT = D / 32, NC = D / 16, NS = 2;
+  __shared__ __attribute__((aligned(1024))) char smem[kWavesT * NS * kStageT];
+  __shared__ float s_m[kWavesT][16], s_l[kWavesT][16], s_t[kWavesT][16];
+  __shared__ int s_over[kWavesT];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int G = a.Hq / a.Hkv;
+  const int n = min(max(a.kv_len[b], 0), a.max_len);
+  const int r0 = split * a.chunk;
+  if (r0 >= n) return;  // beyond this sequence: the combine never reads it
+  const int r1 = min(r0 + a.chunk, n);
+  const int ntile = (r1 - r0 + kRows - 1) / kRows;
+  const int64_t blk = ((int64_t)b * a.Hkv + g) * a.nsplit + split;
+  if (REDO && a.dflags[blk] == 0) return;
+
+  const int64_t srow = ((int64_t)b * a.Hkv + g) * a.cap;   // first cache row of this (b, g)
+  const uint16_t* xbase = a.kc + srow * D;
+  const uint16_t* krbase = a.krc + srow * 128;
+  const float* rbase = a.rc + srow;
+  char* mybuf = smem + wave * NS * kStageT;
+
+  // Q^T (B operand of the 16x16x32 MFMA): lane -> head (lane & 15), dims
+  // 32t + 8(lane >> 4) ..; the non-rotated dims carry the K-norm weight.
+  const int hcol = lane & 15, kq = lane >> 4;
+  const bool hvalid = hcol < G;
+  bf16x8 qf[NT];
+  {
+    const uint16_t* qrow = a.q + ((int64_t)b * a.Hq + g * G + (hvalid ? hcol : 0)) * D;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int d0 = 32 * t + 8 * kq;
+      u32x4 raw = hvalid ? *(const u32x4*)(qrow + d0) : u32x4{0, 0, 0, 0};
+      if (!rot_step32(t)) {
+        const u32x4 w = *(const u32x4*)(a.w_k + d0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) raw[i] = pack_bf2(bf_lo(raw[i]) * bf_lo(w[i]), bf_hi(raw[i]) * bf_hi(w[i]));
+      }
+      qf[t] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
+
+  f32x4 oacc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) oacc[c] = f32x4{};
+  float m_ref = -INFINITY, m_true = -INFINITY, l_part = 0.f;
+  const int64_t hrow = ((int64_t)b * a.Hq + g * G + (hvalid ? hcol : 0)) * a.nsplit + split;
+  if (REDO) m_ref = a.dmax[hrow];
+
+  const int krow = lane & 15;
+  const int k_rowoff = d_row_off<D>(krow), k_x = d_xor(krow);
+  const int tR = 4 * (lane >> 4) + ((lane >> 2) & 3);
+  const int tq = lane & 3;
+  const int tr_off = d_row_off<D>(tR) + (tq & 1) * 8;
+  const int tr_j = (tq >> 1) ^ d_xor(tR);
+
+  // copy of tile tl: 16 X rows, 16 Krot rows (4 loads of 4 rows, each lane's
+  // chunk XOR-swizzled by its row) and the rows' factors (all 64 lanes; 16 used)
+  auto issue = [&](int it) {
+    const int tl = wave + kWavesT * it;
+    char* st = mybuf + (it % NS) * kStageT;
+    const int row0 = r0 + tl * kRows;
+    load_rows<D>(xbase, row0, r1, st, lane);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int R = 4 * j + (lane >> 4);
+      const int row = min(row0 + R, r1 - 1);
+      const int c = (lane & 15) ^ R;
+      g2lds16(krbase + (int64_t)row * 128 + c * 8, (G4_LDS void*)(st + kKrOff + j * 1024));
+    }
+    g2lds4(rbase + min(row0 + lane, r1 - 1), (G4_LDS void*)(st + kROff));
+  };
+  constexpr int LPT = kRows + 4 + 1;  // loads per tile per wave
+  const int nmine = ntile > wave ? (ntile - wave + kWavesT - 1) / kWavesT : 0;
+  if (nmine > 0) issue(0);
+  for (int it = 0; it < nmine; ++it) {
+    wait_vmem<0>();
+    if (it + 1 < nmine) issue(it + 1);  // into the stage tile it-1 used
+    const int tl = wave + kWavesT * it;
+    char* cur = mybuf + (it % NS) * kStageT;
+
+    f32x4 sacc = f32x4{};
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      bf16x8 ka;
+      if (rot_step32(t)) {
+        const int u = t < 2 ? t : t - 6;
+        ka = lds_read_b128((const G4_LDS char*)(cur + kKrOff + krow * 256 + (((4 * u + kq) ^ krow) * 16)));
+      } else {
+        const int ch = (4 * t + kq) ^ k_x;
+        ka = lds_read_b128((const G4_LDS char*)(cur + k_rowoff + ch * 16));
+      }
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[t], sacc, 0, 0, 0);
+    }
+    // lane holds head hcol, keys 4*kq + i of this tile; c = r * scale*log2(e)
+    const f32x4 rv = *(const G4_LDS f32x4*)(cur + kROff + 16 * kq);
+    const int key0 = r0 + tl * kRows + 4 * kq;
+    float s[4], c[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      c[i] = rv[i] * a.scale_log2;
+      s[i] = (key0 + i < r1) ? sacc[i] * c[i] : -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    m_true = fmaxf(m_true, mx);
+    if (!REDO && it == 0) {  // the wave's first tile fixes its reference
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      m_ref = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    }
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e = __builtin_amdgcn_exp2f(s[i] - m_ref);
+      l_part += e;
+      p[i] = e * rv[i];  // value row p is r_p X_p
+    }
+    const u32x2 pw = {pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3])};
+    const i16x4_t pb = __builtin_bit_cast(i16x4_t, pw);
+#pragma unroll
+    for (int cb = 0; cb < NC; ++cb) {
+      const i16x4 va = lds_read_tr16((const G4_LDS char*)(cur + tr_off + (2 * cb + tr_j) * 16));
+      oacc[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, oacc[cb], 0, 0, 0);
+    }
+  }
+  (void)LPT;
+
+  // ---- merge the waves' partial states (each relative to its own reference)
+  float l_tot = l_part + __shfl_xor(l_part, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  float mt = fmaxf(m_true, __shfl_xor(m_true, 16, 64));
+  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+  if (lane < 16) { s_m[wave][lane] = m_ref; s_l[wave][lane] = l_tot; s_t[wave][lane] = mt; }
+  if (lane == 0) s_over[wave] = __builtin_amdgcn_ballot_w64(hvalid && mt > m_ref + kHeadroom) != 0;
+  __syncthreads();  // all waves are done with their tiles; reuse LDS for O
+  float* so = (float*)smem;  // [kWavesT][16 heads][D]
+  if (hvalid) {
+#pragma unroll
+    for (int cb = 0; cb < NC; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) so[(wave * 16 + hcol) * D + 16 * cb + 4 * kq + i] = oacc[cb][i];
+  }
+  if (!REDO && threadIdx.x == 0) {
+    int over = 0;
+#pragma unroll
+    for (int w = 0; w < kWavesT; ++w) over |= s_over[w];
+    a.dflags[blk] = over;
+  }
+  if (!REDO && threadIdx.x < G) {
+    float t = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWavesT; ++w) t = fmaxf(t, s_t[w][threadIdx.x]);
+    a.dmax[((int64_t)b * a.Hq + g * G + threadIdx.x) * a.nsplit + split] = t;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * D; idx += kWavesT * 64) {
+    const int hh = idx / D, d = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWavesT; ++w) M = fmaxf(M, s_m[w][hh]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWavesT; ++w) {
+      const float wt = s_m[w][hh] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s_m[w][hh] - M);
+      L += wt * s_l[w][hh];
+      O += wt * so[(w * 16 + hh) * D + d];
+    }
+    const int64_t ph = (int64_t)b * a.Hq + g * G + hh;
+    a.o_part[(ph * a.nsplit + split) * D + d] = O / L;
+    if (d == 0) a.lse_part[ph * a.nsplit + split] = (M + __log2f(L)) * kLn2;
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   const int h = blockIdx.x, b = blockIdx.y;
@@ -280,6 +472,18 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+hipError_t launch_decode_tied(const DecodeArgs& a, hipStream_t st) {
+  const dim3 grid(a.nsplit, a.Hkv, a.B);
+  hipLaunchKernelGGL(decode_tied_kernel<false>, grid, dim3(kWavesT * 64), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_tied_kernel<true>, grid, dim3(kWavesT * 64), 0, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<512>), dim3(a.Hq, a.B), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   const bool same = a.kc == a.vc;

@@ -137,8 +137,11 @@ hipError_t launch_norm_rope(const NormRopeArgs& a, hipStream_t st);
 struct KvPrepArgs {         // K=V prefill pre-pass
   const uint16_t* x;        // [B, S, Hkv, 512] strided
   const uint16_t* w_k;      // [512]
-  float* r;                 // [B, Hkv, S] inverse RMS of each row times rscale
-  uint16_t* krot;           // [B, Hkv, S, 128]
+  float* r;                 // [B, Hkv, S | cap] inverse RMS of each row times rscale
+  uint16_t* krot;           // [B, Hkv, S | cap, 128]
+  uint16_t* x_out;          // cache mode: [B, Hkv, cap, 512] copy of X, else NULL
+  const int32_t* pos0;      // cache mode: [B] first position (NULL = 0)
+  int cap;                  // 0: prefill layout; > 0: cache rows pos0[b] + t
   int B, S, Hkv, rot;
   float rscale;
   double log2_theta;
@@ -183,7 +186,12 @@ struct DecodeArgs {
   int B, Hq, Hkv, D, cap, nsplit, chunk;
   int max_len;              // host bound; kv_len values are clamped to [0, max_len]
   float scale_log2;
+  // K=V decode over the raw projection (kc = X cache; vc unused):
+  const float* rc;          // [B, Hkv, cap] inverse RMS of each cached row
+  const uint16_t* krc;      // [B, Hkv, cap, 128] rotated part of each cached key, before r
+  const uint16_t* w_k;      // [512] K-norm weight
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_decode_tied(const DecodeArgs& a, hipStream_t st);
 
 }  // namespace g4attn

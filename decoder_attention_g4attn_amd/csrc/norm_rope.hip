@@ -121,7 +121,9 @@ __global__ __launch_bounds__(256) void norm_rope_kernel(NormRopeArgs a) {
   }
 }
 
-// K=V pre-pass on the raw tied projection X (D = 512, 128 rotated dims):
+// K=V pre-pass on the raw tied projection X (D = 512, 128 rotated dims),
+// for the prefill (rows t of [B, Hkv, S]) or appending to a decode cache
+// (rows pos0[b] + t of [B, Hkv, cap], X copied into its cache as well):
 //   r[b,g,t]      = rscale / sqrt(mean_d X^2 + eps)   (the inverse RMS, with
 //                   the logit scale folded in by the caller)
 //   krot[b,g,t,:] = RoPE_t(X * w_k) on dims 0..63 and 256..319 (no r)
@@ -134,6 +136,11 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(KvPrepArgs a) {
   if (tok >= (int64_t)a.B * a.S) return;
   const int b = (int)(tok / a.S);
   const int t = (int)(tok % a.S);
+  // prefill layout: row t of [B, Hkv, S]; cache layout: row p = pos0[b] + t
+  // of [B, Hkv, cap], with the raw row copied into the X cache too
+  const int p = a.cap ? (a.pos0 ? a.pos0[b] : 0) + t : t;
+  if (a.cap && (p < 0 || p >= a.cap)) return;
+  const int nrows = a.cap ? a.cap : a.S;
   const int j0 = E * lane;
   const int live = a.rot / 2;  // 64
   const bool rot_lane = j0 < live;
@@ -142,7 +149,7 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(KvPrepArgs a) {
   for (int e = 0; e < E; ++e) {
     if (rot_lane) {
       const double f = exp2(-2.0 * (double)(j0 + e) / (double)D * a.log2_theta);
-      rope_angle((double)t, f, c[e], s[e]);
+      rope_angle((double)p, f, c[e], s[e]);
     } else {
       c[e] = 1.f; s[e] = 0.f;
     }
@@ -158,8 +165,12 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(KvPrepArgs a) {
 #pragma unroll
     for (int e = 0; e < E; ++e) ss += lo[e] * lo[e] + hi[e] * hi[e];
     ss = wave_sum(ss);
-    const int64_t row = ((int64_t)b * a.Hkv + g) * a.S + t;
+    const int64_t row = ((int64_t)b * a.Hkv + g) * nrows + p;
     if (lane == 0) a.r[row] = a.rscale / sqrtf(ss / (float)D + a.eps);
+    if (a.x_out) {
+      Vec<E>::store(a.x_out + row * D + j0, lo);    // exact: bf16 in, bf16 out
+      Vec<E>::store(a.x_out + row * D + HALF + j0, hi);
+    }
     if (rot_lane) {
       float ylo[E], yhi[E];
 #pragma unroll

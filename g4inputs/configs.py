@@ -76,6 +76,12 @@ WORKLOADS = {
         "31b_sliding_image_prefill", 8, "prefill", B=2, S=16384, Hq=32, Hkv=16, D=256,
         window=1024, rotary_dims=256, theta=1e4, k_eq_v=False,
         images=tuple((1000 + 1900 * i, 280) for i in range(8))),
+    # the 31B K=V decode over the layer's own cache format: raw projection
+    # rows plus their inverse RMS and rotated key part (V unroped)
+    "31b_global_kv_decode_raw": Workload(
+        "31b_global_kv_decode_raw", 9, "decode", B=32, S=1, Hq=32, Hkv=4, D=512,
+        window=0, rotary_dims=128, theta=1e6, k_eq_v=True,
+        len_lo=32768, len_hi=131072),
     # sliding-layer decode of the same 31B batch over rolling caches
     "31b_sliding_decode": Workload(
         "31b_sliding_decode", 6, "decode", B=32, S=1, Hq=32, Hkv=16, D=256,

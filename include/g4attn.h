@@ -9,7 +9,9 @@
  *   g4attn_prefill_chunk - the same for a chunk of new positions over
  *                       caches (chunked prefill, padded batches);
  *   g4attn_decode     - one new query token per sequence over a KV cache
- *                       (split-KV plus a log-sum-exp combine).
+ *                       (split-KV plus a log-sum-exp combine);
+ *   g4attn_kv_tied_append, g4attn_decode_tied - a K=V global layer's cache
+ *                       of its raw projection, and decode over it.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -257,6 +259,49 @@ g4attn_status g4attn_decode(const g4attn_layer_desc* desc, const g4attn_bf16* q,
                             const int32_t* kv_len, int32_t B, int32_t max_kv_len,
                             int32_t cache_cap, g4attn_bf16* out, float* lse, int32_t num_splits,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Append rows to a K=V global layer's own cache: the raw tied projection X
+ * ("Gemma 4" docs, "What changed from Gemma 3", K=V global MQA: K =
+ * RoPE(RMSNorm(X) w_k), V = RMSNorm(X), weightless) is cached as X itself
+ * plus, per row, its inverse RMS r and the rotated part of its key before
+ * r, so that the decode below forms K and V exactly (V unroped):
+ *
+ *   p = (pos0 ? pos0[b] : 0) + t
+ *   x_cache[b,g,p,:]    = X[b,t,g,:]                              (copied)
+ *   r_cache[b,g,p]      = 1 / sqrt(mean_d X[b,t,g,d]^2 + rms_eps)
+ *   krot_cache[b,g,p,:] = RoPE_p(X[b,t,g,:] * w_k) on dims 0..63, 256..319
+ *
+ *   x          [B, S, Hkv, 512] raw projection, strides x_strides.
+ *   w_k        [512] K-norm weight; rotary_dims must be 128 (0.25 of 512).
+ *   x_cache    [B, Hkv, cache_cap, 512] bf16; r_cache [B, Hkv, cache_cap]
+ *   r_cache,   fp32; krot_cache [B, Hkv, cache_cap, 128] bf16; all
+ *   krot_cache contiguous.
+ *   pos0, max_pos  as in g4attn_norm_rope (max_pos >= cache_cap is
+ *              G4ATTN_ERR_CACHE_OVERFLOW).
+ */
+g4attn_status g4attn_kv_tied_append(const g4attn_bf16* x, const g4attn_bf16* w_k, int32_t B, int32_t S,
+                                    int32_t Hkv, int32_t rotary_dims, float rope_theta, float rms_eps,
+                                    const int64_t x_strides[3], const int32_t* pos0, int32_t max_pos,
+                                    g4attn_bf16* x_cache, float* r_cache, g4attn_bf16* krot_cache,
+                                    int32_t cache_cap, void* stream);
+
+/*
+ * Decode of a K=V global layer over the cache g4attn_kv_tied_append writes:
+ * out and lse as in g4attn_decode with, for cached row p,
+ *   K_p = r_p * (X_p * w_k on the unrotated dims | krot_p on the rotated)
+ *   V_p = r_p * X_p
+ * (the keys of the prefill's K=V path).  1284 bytes per cached row and KV
+ * head are read once.  desc: k_eq_v = 1, head_dim 512, rotary_dims 128,
+ * window 0 (else G4ATTN_ERR_UNSUPPORTED).  q, kv_len, max_kv_len,
+ * cache_cap, out, lse, num_splits and the workspace as in g4attn_decode
+ * (g4attn_decode_workspace_bytes gives its size).
+ */
+g4attn_status g4attn_decode_tied(const g4attn_layer_desc* desc, const g4attn_bf16* q, const g4attn_bf16* x_cache,
+                                 const float* r_cache, const g4attn_bf16* krot_cache, const g4attn_bf16* w_k,
+                                 const int32_t* kv_len, int32_t B, int32_t max_kv_len, int32_t cache_cap,
+                                 g4attn_bf16* out, float* lse, int32_t num_splits, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* g4attn_status_str(g4attn_status status);

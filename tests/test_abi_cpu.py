@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert g4.g4attn_version() == 300
+    assert g4.g4attn_version() == 400
     for s in range(8):
         assert g4.g4attn_status_str(s)
     assert g4.load().g4attn_last_hip_error() == 0
@@ -138,6 +138,32 @@ def test_prefill_chunk_validation():
     assert call(S=0) == g4.ERR_SHAPE
     assert call(q=MISALIGNED) == g4.ERR_LAYOUT
     assert call() == g4.ERR_WORKSPACE
+
+
+def test_kv_tied_cache_validation():
+    lib = g4.load()
+    xs = I64(16 * 4 * 512, 4 * 512, 512)
+
+    def append(x=FAKE, wk=FAKE, rot=128, pos0=None, max_pos=15, cap=64, S=16):
+        return lib.g4attn_kv_tied_append(x, wk, 1, S, 4, rot, 1e6, 1e-6, xs, pos0, max_pos, FAKE, FAKE, FAKE,
+                                         cap, None)
+
+    assert append(wk=None) == g4.ERR_NULL
+    assert append(rot=256) == g4.ERR_UNSUPPORTED
+    assert append(cap=15) == g4.ERR_CACHE_OVERFLOW
+    assert append(pos0=FAKE, max_pos=10) == g4.ERR_SHAPE
+    assert append(x=MISALIGNED) == g4.ERR_LAYOUT
+
+    def decode(desc, max_len=100, cap=128, ws=FAKE, wsb=1 << 30, wk=FAKE):
+        return lib.g4attn_decode_tied(ctypes.byref(desc), FAKE, FAKE, FAKE, FAKE, wk, FAKE, 2, max_len, cap, FAKE,
+                                      None, 0, ws, wsb, None)
+
+    kv = _desc(k_eq_v=True)
+    assert decode(kv, wk=None) == g4.ERR_NULL
+    assert decode(_desc()) == g4.ERR_UNSUPPORTED                      # not a K=V layer
+    assert decode(_desc(k_eq_v=True, window=16)) == g4.ERR_UNSUPPORTED
+    assert decode(kv, max_len=200) == g4.ERR_CACHE_OVERFLOW
+    assert decode(kv, ws=None) == g4.ERR_WORKSPACE
 
 
 def test_decode_ring_workspace_uses_window_rows():

@@ -172,3 +172,35 @@ def test_full_size_chunk_prefill_sampled_rows(gpu_lib):
                     got_all.append(f64(s["out"][b, t, h]))
                     np.testing.assert_allclose(float(lse[b, h, t]), m + np.log(e.sum()), rtol=0, atol=LSE_ATOL)
     assert_parity(np.stack(got_all), np.stack(ref_all), "31b sliding chunk prefill sampled rows")
+
+
+def test_full_size_raw_kv_decode_sampled_heads(gpu_lib):
+    """The 31B K=V decode over the raw-projection cache (X + r + Krot), as timed."""
+    g4 = gpu_lib
+    c = WORKLOADS["31b_global_kv_decode_raw"]
+    s = bench.build_decode_raw(torch, g4, gen, c)
+    lse = torch.empty((c.B, c.Hq), dtype=torch.float32, device="cuda")
+    bench.run_decode_pro(g4, s)
+    g4.g4attn_decode_tied(s["desc"], s["q"].view(c.B, c.Hq, c.D), s["xc"], s["rc"], s["krc"], s["wk"], s["kv_len"],
+                          s["max_len"], s["out"], lse=lse, workspace=s["ws"])
+    torch.cuda.synchronize()
+    L, n = s["L"], s["n"]
+    order = np.argsort(n)
+    batch = sorted({int(order[0]), int(order[-1]), 7})
+    heads = [0, 7, 8, 31]
+    G = c.Hq // c.Hkv
+    got, ref = [], []
+    for b in batch:
+        q = onr.norm_rope(f64(s["q_raw"][b:b + 1]), f64(s["wq"]), np.array([[L[b]]]), c.rotary_dims, c.theta)
+        for g in sorted({h // G for h in heads}):
+            X = f64(s["xc"][b, g, :int(n[b])])[None, :, None, :]          # [1, n, 1, D] raw rows
+            K, V = onr.kv_tied_k_v(X, f64(s["wk"]), np.arange(int(n[b]))[None, :], c.rotary_dims, c.theta)
+            kk, vv = K[0, :, 0], V[0, :, 0]
+            for h in [h for h in heads if h // G == g]:
+                sc = c.scale * (kk @ q[0, 0, h])
+                m = sc.max()
+                e = np.exp(sc - m)
+                ref.append((e @ vv) / e.sum())
+                got.append(f64(s["out"][b, h]))
+                np.testing.assert_allclose(float(lse[b, h]), m + np.log(e.sum()), rtol=0, atol=LSE_ATOL)
+    assert_parity(np.stack(got), np.stack(ref), "31B raw K=V decode sampled heads")
