@@ -99,3 +99,27 @@ def test_decode_tied_equals_prefill_last_row(gpu_lib):
                           torch.tensor([S], dtype=torch.int32, device=DEV), S, out)
     torch.cuda.synchronize()
     assert_parity(f64(out[0]), f64(pre[0, S - 1]), "K=V decode vs prefill last row")
+
+
+def test_kv_shared_layers_reuse_one_cache(gpu_lib):
+    """KV-shared layers: a later layer decodes over an earlier layer's caches by passing the same
+    tensors; the result is bit-identical to decoding over private copies, and the shared caches
+    are left untouched."""
+    g4 = gpu_lib
+    B, Hq, Hkv, Dh, cap = 3, 8, 2, 256, 600
+    lens = torch.tensor([5, 333, 600], dtype=torch.int32, device=DEV)
+    kc, vc = _bf((B, Hkv, cap, Dh), 30), _bf((B, Hkv, cap, Dh), 31)
+    before = (kc.clone(), vc.clone())
+    desc = g4.layer_desc(Hq, Hkv, Dh, rotary_dims=Dh)
+    outs = []
+    for layer in range(2):                               # two layers, one pair of caches
+        q = _bf((B, Hq, Dh), 40 + layer)
+        shared = torch.empty((B, Hq, Dh), dtype=torch.bfloat16, device=DEV)
+        private = torch.empty_like(shared)
+        g4.g4attn_decode(desc, q, kc, vc, lens, cap, shared)
+        g4.g4attn_decode(desc, q, kc.clone(), vc.clone(), lens, cap, private)
+        torch.cuda.synchronize()
+        assert torch.equal(shared, private)
+        outs.append(shared)
+    assert torch.equal(kc, before[0]) and torch.equal(vc, before[1])
+    assert not torch.equal(outs[0], outs[1])
