@@ -332,7 +332,6 @@ __global__ __launch_bounds__(kWavesT * 64) void decode_tied_kernel(DecodeArgs a)
     }
     g2lds4(rbase + min(row0 + lane, r1 - 1), (G4_LDS void*)(st + kROff));
   };
-  constexpr int LPT = kRows + 4 + 1;  // loads per tile per wave
   const int nmine = ntile > wave ? (ntile - wave + kWavesT - 1) / kWavesT : 0;
   if (nmine > 0) issue(0);
   for (int it = 0; it < nmine; ++it) {
@@ -384,7 +383,6 @@ __global__ __launch_bounds__(kWavesT * 64) void decode_tied_kernel(DecodeArgs a)
       oacc[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, oacc[cb], 0, 0, 0);
     }
   }
-  (void)LPT;
 
   // ---- merge the waves' partial states (each relative to its own reference)
   float l_tot = l_part + __shfl_xor(l_part, 16, 64);

@@ -12,11 +12,15 @@
 //     a KV head share every K/V tile the workgroup loads.
 //   * Each wave owns 32 rows.  It computes S^T = K Q^T and O^T = V^T P^T with
 //     v_mfma_f32_32x32x16_bf16: lane l holds query row l%32 in both results,
-//     so the online softmax is per lane plus one partner lane (l ^ 32).
-//     Q^T stays in registers (D/4 VGPRs), O^T accumulates in D/2 registers.
-//   * K/V tiles of 32 keys are double-buffered in LDS with direct
-//     global->LDS loads; tiles wholly outside the causal/window band are
-//     never visited and only edge tiles are masked element by element.
+//     so the softmax is per lane plus one partner lane (l ^ 32).  Q^T stays
+//     in registers (D/4 VGPRs), O^T accumulates in D/2 registers.
+//   * K/V tiles of 32 keys stream through an LDS ring (three stages where
+//     they fit) with direct global->LDS loads; tiles wholly outside the
+//     causal/window band are never visited and only edge tiles are masked
+//     element by element.
+//   * prefill_kernel software-pipelines one wave per SIMD (D = 512);
+//     prefill_d256_kernel runs two waves per SIMD (D = 256).  Both also take
+//     chunked rows over caches and bidirectional spans (the EXT variant).
 //
 // K=V global layers (D = 512): keys are RoPE(RMS(X) w_k), values RMS(X), from
 // one raw tensor X.  With r_p the inverse RMS of key row p and R the rotated
@@ -189,11 +193,6 @@ __device__ __forceinline__ void wg_map(int T, int Hkv, int& b, int& g, int& tile
   tile = T - 1 - r;  // heaviest (latest) rows first
 }
 
-// Scheduling-group masks (LLVM AMDGPU): VALU (incl. transcendental), MFMA,
-// LDS read.
-constexpr int kSgValu = 0x402;
-constexpr int kSgMfma = 0x008;
-constexpr int kSgDsRead = 0x100;
 constexpr int kLook = 3;  // LDS operand reads issued ahead of their MFMA
 
 // O^T block += V^T P^T on the AGPR accumulator.  Written as assembly so that
