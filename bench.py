@@ -88,6 +88,34 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read_per_launch": n, "copy_bytes_written_per_launch": n, "launches": 3}))
 
 
+def attainable(torch):
+    """Measured attainable rates on this GPU, as context for the roofline
+    fractions: a plain device copy of 2 GiB (read + write bytes over time)
+    and a large bf16 GEMM through torch (the vendor library's MFMA path)."""
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+    n = 2 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    ms = timed(lambda: dst.copy_(src), 5)
+    copy_gbps = 2.0 * n / ms / 1e6
+    del src, dst
+    m = 8192
+    a = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    b = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    ms = timed(lambda: torch.matmul(a, b), 5)
+    gemm = 2.0 * m ** 3 / ms / 1e9
+    return {"hbm_copy_GBps": round(copy_gbps, 1), "bf16_gemm_8192_tflops": round(gemm, 1)}
+
+
 class Stage:
     def __init__(self, name):
         self.name = name
@@ -465,6 +493,12 @@ def main():
         "stage_ms_min": {k: round(v, 4) for k, v in mins.items()},
         "roofline": roof,
     }
+    if args.only is None:
+        log("measuring attainable copy and GEMM rates")
+        att = attainable(torch)
+        att["global_prefill_frac_of_gemm"] = round(res["global_prefill_tflops"] / att["bf16_gemm_8192_tflops"], 4)
+        att["decode_frac_of_copy"] = round(res["decode_GBps"] / att["hbm_copy_GBps"], 4)
+        out["attainable"] = att
     if not args.no_cpu_baseline and "global_attn" in avg:
         log("timing the CPU oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(torch, gen, st)
