@@ -41,9 +41,9 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 # change, the roofline reports traffic as null until the counters are re-taken.
 PREFILL_TRAFFIC = {
     "sources": ["prefill.hip", "g4attn_internal.h", "norm_rope.hip", "abi.hip"],
-    "sources_sha256": "1bc99a2ccdcbe3c169aeaef4967c86d798a278f5c10d56890aee655d72d0e89d",
-    "fetch_kib": 3.24633e6, "fetch_scale": 2.0,
-    "write_kib": 2.04194e6, "write_scale": 1.0,
+    "sources_sha256": "ace6c149a5d75a07f5a1aacc57e1b3a9ee1edfcbd517b1e764743cc09b4fa70a",
+    "fetch_kib": 3.24762e6, "fetch_scale": 2.0,
+    "write_kib": 2.00135e6, "write_scale": 1.0,
 }
 
 
