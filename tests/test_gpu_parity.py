@@ -325,3 +325,32 @@ def test_decode_reference_overflow_redo(gpu_lib, same):
     ro, rl = oat.decode_attention(f64(q), k64, k64 if same else f64(vc), kv_len.cpu().numpy(), desc.scale)
     assert_parity(f64(out), ro, f"decode redo same={same}")
     np.testing.assert_allclose(lse.cpu().numpy(), rl, rtol=1e-5, atol=2e-3)
+
+
+def _random_configs(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        D = int(rng.choice([256, 512]))
+        Hkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.choice([1, 2, 3, 8]))
+        S = int(rng.integers(1, 420))
+        w = int(rng.choice([0, 0, 1, 17, 64, 300]))
+        B = int(rng.integers(1, 3))
+        out.append((B, S, G * Hkv, Hkv, D, w))
+    return out
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,D,w", _random_configs(12, 2024))
+def test_prefill_random_configs_vs_oracle(gpu_lib, B, S, Hq, Hkv, D, w):
+    """Seeded random shapes: lengths, windows, head groupings and widths drawn together."""
+    g4 = gpu_lib
+    q, k, v = _bf((B, S, Hq, D), 900 + S), _bf((B, S, Hkv, D), 901 + S), _bf((B, S, Hkv, D), 902 + S)
+    desc = g4.layer_desc(Hq, Hkv, D, window=w, rotary_dims=D)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=DEV)
+    g4.g4attn_prefill(desc, q, k, v, out, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = oat.attention_band(f64(q), f64(k), f64(v), desc.scale, w)
+    assert_parity(f64(out), ro, f"random B={B} S={S} Hq={Hq} Hkv={Hkv} D={D} w={w}")
+    np.testing.assert_allclose(lse.cpu().numpy(), rl, rtol=0, atol=2e-3)
