@@ -45,6 +45,15 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Exchange between lane halves (v_permlane32_swap): lanes 0..31 get their
+// own `a` and their partner's `a`, lanes 32..63 their partner's `b` and
+// their own `b`.  The results as {first, second} of each lane.
+__device__ __forceinline__ void half_swap(uint32_t a, uint32_t b, uint32_t& first, uint32_t& second) {
+  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  first = r[0];
+  second = r[1];
+}
+
 // Wave-wide (64 lanes) reductions.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -623,14 +623,24 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       // K=V: P carried the factor c = r * scale*log2(e) / qmul; omul undoes it.
       const float inv = l_tot > 0.f ? (TIED ? a.omul : 1.f) / l_tot : 0.f;
       uint16_t* orow = a.out + b * a.os[0] + (int64_t)tq * a.os[1] + head * a.os[2];
+      // 16-byte stores: a lane holds dims 8gq + 4hh .. +3 of its row; the two
+      // lane halves trade so that each writes 8 consecutive dims (lanes
+      // 0..31 the even gq, lanes 32..63 the odd one)
 #pragma unroll
       for (int c = 0; c < C::NC; ++c) {
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          u32x2 w;
-          w[0] = pack_bf2(oacc[c][4 * gq + 0] * inv, oacc[c][4 * gq + 1] * inv);
-          w[1] = pack_bf2(oacc[c][4 * gq + 2] * inv, oacc[c][4 * gq + 3] * inv);
-          *(u32x2*)(orow + 32 * c + 8 * gq + 4 * hh) = w;
+        for (int gp = 0; gp < 2; ++gp) {
+          uint32_t pk[2][2];
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const int gq = 2 * gp + k;
+            pk[k][0] = pack_bf2(oacc[c][4 * gq + 0] * inv, oacc[c][4 * gq + 1] * inv);
+            pk[k][1] = pack_bf2(oacc[c][4 * gq + 2] * inv, oacc[c][4 * gq + 3] * inv);
+          }
+          uint32_t x0, x1, x2, x3;
+          half_swap(pk[0][0], pk[1][0], x0, x2);
+          half_swap(pk[0][1], pk[1][1], x1, x3);
+          *(u32x4*)(orow + 32 * c + 8 * (2 * gp + hh)) = u32x4{x0, x1, x2, x3};
         }
       }
       if (a.lse && hh == 0) {
@@ -880,14 +890,24 @@ void prefill_d256_kernel(PrefillArgs a) {
     if (valid) {
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
       uint16_t* orow = a.out + b * a.os[0] + (int64_t)tq * a.os[1] + head * a.os[2];
+      // 16-byte stores: a lane holds dims 8gq + 4hh .. +3 of its row; the two
+      // lane halves trade so that each writes 8 consecutive dims (lanes
+      // 0..31 the even gq, lanes 32..63 the odd one)
 #pragma unroll
       for (int c = 0; c < C::NC; ++c) {
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          u32x2 w;
-          w[0] = pack_bf2(oacc[c][4 * gq + 0] * inv, oacc[c][4 * gq + 1] * inv);
-          w[1] = pack_bf2(oacc[c][4 * gq + 2] * inv, oacc[c][4 * gq + 3] * inv);
-          *(u32x2*)(orow + 32 * c + 8 * gq + 4 * hh) = w;
+        for (int gp = 0; gp < 2; ++gp) {
+          uint32_t pk[2][2];
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const int gq = 2 * gp + k;
+            pk[k][0] = pack_bf2(oacc[c][4 * gq + 0] * inv, oacc[c][4 * gq + 1] * inv);
+            pk[k][1] = pack_bf2(oacc[c][4 * gq + 2] * inv, oacc[c][4 * gq + 3] * inv);
+          }
+          uint32_t x0, x1, x2, x3;
+          half_swap(pk[0][0], pk[1][0], x0, x2);
+          half_swap(pk[0][1], pk[1][1], x1, x3);
+          *(u32x4*)(orow + 32 * c + 8 * (2 * gp + hh)) = u32x4{x0, x1, x2, x3};
         }
       }
       if (a.lse && hh == 0) {
