@@ -146,7 +146,8 @@ size_t g4attn_prefill_workspace_bytes(const g4attn_layer_desc* desc, int32_t B, 
  *              strides kv_strides; v must be NULL; w_k [D] the K-norm weight.
  *              Keys are RoPE(RMSNorm(X) * w_k) at positions 0..S-1 and
  *              values are RMSNorm(X) (weightless), both formed inside the
- *              call from one shared tile of X.  head_dim must be 512.
+ *              call from one shared tile of X.  head_dim must be 512,
+ *              rotary_dims 128, |scale| <= 2^30 (else G4ATTN_ERR_UNSUPPORTED).
  *   out        [B, S, Hq, D] bf16, strides o_strides.
  *   lse        [B, Hq, S] fp32 (contiguous) or NULL.
  *   span_lo,   NULL, or device int32 [B, S]: a bidirectional span per row
