@@ -80,3 +80,36 @@ def test_prefill_chunks_equal_whole_prefill(gpu_lib, D, w):
     # and both against the oracle on the last chunk
     ro, _ = oat.attention_band(f64(q), f64(k), f64(v), desc.scale, w, rows=np.arange(200, 300))
     assert_parity(f64(parts[:, 200:]), ro, f"last chunk vs oracle D={D} w={w}")
+
+
+@pytest.mark.parametrize("D,w", [(256, 0), (256, 96), (512, 0)])
+def test_prefill_chunk_reference_overflow_redo(gpu_lib, D, w):
+    """The extended variant's recompute pass: chunked rows whose logits grow far past their
+    first tile's maximum (q = e_0, k_j = j/2 e_0, scale 1), with bidirectional spans too."""
+    g4 = gpu_lib
+    B, Hq, Hkv, total, chunk = 1, 8, 1, 300, 100
+    P = total - chunk
+    q = torch.zeros((B, chunk, Hq, D), dtype=torch.bfloat16, device=DEV)
+    q[..., 0] = 1.0
+    j = torch.arange(total, device=DEV, dtype=torch.float32)
+    kc = torch.zeros((B, Hkv, total, D), dtype=torch.bfloat16, device=DEV)
+    kc[0, 0, :, 0] = (0.5 * j).to(torch.bfloat16)
+    vc = _bf((B, Hkv, total, D), 70)
+    desc = g4.layer_desc(Hq, Hkv, D, window=w, scale=1.0)
+    lo, hi = gen.image_spans(total, [(230, 40)])
+    slo = torch.from_numpy(lo[P:][None]).to(DEV)
+    shi = torch.from_numpy(hi[P:][None]).to(DEV)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, chunk), dtype=torch.float32, device=DEV)
+    g4.g4attn_prefill_chunk(desc, q, kc, vc, out, torch.tensor([P], dtype=torch.int32, device=DEV),
+                            torch.tensor([chunk], dtype=torch.int32, device=DEV), total - 1, lse=lse,
+                            span_lo=slo, span_hi=shi)
+    torch.cuda.synchronize()
+    qf = torch.zeros((B, total, Hq, D), dtype=torch.float64)
+    qf[:, P:] = torch.from_numpy(f64(q))
+    kf = f64(kc).transpose(0, 2, 1, 3)
+    vf = f64(vc).transpose(0, 2, 1, 3)
+    m = oat.mask_spans(total, w, lo, hi)
+    ro, rl = oat.attention_masked(qf.numpy(), kf, vf, 1.0, m)
+    assert_parity(f64(out), ro[:, P:], f"chunk redo D={D} w={w}")
+    np.testing.assert_allclose(lse.cpu().numpy(), rl[:, :, P:], rtol=1e-4, atol=2e-3)
