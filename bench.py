@@ -41,9 +41,9 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 # change, the roofline reports traffic as null until the counters are re-taken.
 PREFILL_TRAFFIC = {
     "sources": ["prefill.hip", "g4attn_internal.h", "norm_rope.hip", "abi.hip"],
-    "sources_sha256": "ace6c149a5d75a07f5a1aacc57e1b3a9ee1edfcbd517b1e764743cc09b4fa70a",
-    "fetch_kib": 3.24762e6, "fetch_scale": 2.0,
-    "write_kib": 2.00135e6, "write_scale": 1.0,
+    "sources_sha256": "9f2812a110fbee1ff18fc6febc7452cad9e40226f72bccf90ff6f153001defb5",
+    "fetch_kib": 3.23952e6, "fetch_scale": 2.0,
+    "write_kib": 1.26393e6, "write_scale": 1.0,
 }
 
 
