@@ -745,14 +745,17 @@ void prefill_d256_kernel(PrefillArgs a) {
           g2lds16s(which ? ts.v : ts.k, off, stage + which * C::KT_BYTES + s * kSeg);
         }
     };
-    load_tile_w(lds0, kt_lo);
-
+    // Q^T first, then the first two tiles: the first tile's wait then leaves
+    // the second one's copies in flight (vector-memory counts retire in order)
     bf16x8 qf[C::NT];
     {
       const uint16_t* qrow = a.q + b * a.qs[0] + (int64_t)min(tq, a.S - 1) * a.qs[1] + head * a.qs[2];
 #pragma unroll
       for (int t = 0; t < C::NT; ++t) qf[t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * t + 8 * hh));
     }
+    constexpr int kLoadsPerTile = 2 * (16 / NW);  // this wave's copies of one K/V tile
+    load_tile_w(lds0, kt_lo);
+    if (kt_lo < kt_hi) load_tile_w(lds0 + C::STAGE, kt_lo + 1);
 
     const int k_x = kv_xor<D>(lr);
     const uint32_t koff0 = kv_row_off<D>(lr) + 16 * (hh ^ k_x);
@@ -816,13 +819,14 @@ void prefill_d256_kernel(PrefillArgs a) {
       for (int kt = kt_lo; kt <= kt_hi; ++kt) {
         wait_vmem_all();
         __syncthreads();
-        if (kt < kt_hi) load_tile_w(lds0 + (C::STAGE - so), kt + 1);
+        if (kt > kt_lo && kt < kt_hi) load_tile_w(lds0 + (C::STAGE - so), kt + 1);
         m_run = fmaxf(m_run, tile_max(qk(so), kt));
         so = C::STAGE - so;
       }
       m_ref = max_xor32(m_run);
       __syncthreads();
       load_tile_w(lds0, kt_lo);
+      if (kt_lo < kt_hi) load_tile_w(lds0 + C::STAGE, kt_lo + 1);
     }
 
     f32x16 oacc[C::NC];
@@ -830,9 +834,13 @@ void prefill_d256_kernel(PrefillArgs a) {
     for (int c = 0; c < C::NC; ++c) oacc[c] = f32x16{};
     int so = 0;
     for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-      wait_vmem_all();  // this wave's copies of tile kt have landed
+      // this wave's copies of tile kt have landed (at kt_lo those of kt_lo+1 may not have)
+      if (kt == kt_lo && kt_lo < kt_hi)
+        wait_vmem<kLoadsPerTile>();
+      else
+        wait_vmem_all();
       __syncthreads();  // all of tile kt is in LDS; every wave is done with tile kt-1
-      if (kt < kt_hi) load_tile_w(lds0 + (C::STAGE - so), kt + 1);
+      if (kt > kt_lo && kt < kt_hi) load_tile_w(lds0 + (C::STAGE - so), kt + 1);
       f32x16 s = qk(so);
       if (!REDO && __builtin_amdgcn_ballot_w64(m_ref == -INFINITY)) {
         const float rowmx = max_xor32(tile_max(s, kt));
