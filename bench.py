@@ -288,6 +288,13 @@ def run_image_attn(g4, s):
                       span_hi=s["span_hi"])
 
 
+def visible_pairs(S, window):
+    """Visible (row, key) pairs of one head: row i sees min(i+1, w) keys (all i+1 if global)."""
+    if window == 0 or S <= window:
+        return S * (S + 1) // 2
+    return window * (window + 1) // 2 + (S - window) * window
+
+
 def span_pairs(S, window, lo, hi):
     """Visible (row, key) pairs of one head with bidirectional spans [lo, hi]:
     the window's (or causal) keys plus each row's span keys outside them."""
@@ -423,8 +430,8 @@ def main():
     mins = {k: float(np.min(v)) for k, v in ms.items()}
 
     cs, cg, cd = st["sliding"]["c"], st["global"]["c"], st["decode"]["c"]
-    fl_sliding = 4.0 * cs.D * g4.visible_pairs(cs.S, cs.window) * cs.Hq * cs.B
-    fl_global = 4.0 * cg.D * g4.visible_pairs(cg.S, 0) * cg.Hq * cg.B
+    fl_sliding = 4.0 * cs.D * visible_pairs(cs.S, cs.window) * cs.Hq * cs.B
+    fl_global = 4.0 * cg.D * visible_pairs(cg.S, 0) * cg.Hq * cg.B
     dec = st["decode"]
     dec_bytes = float(dec["n"].sum()) * cd.Hkv * cd.D * 2 + 2.0 * cd.B * cd.Hq * cd.D * 2
     sdec, csd = st["sdecode"], st["sdecode"]["c"]

@@ -138,6 +138,18 @@ def _check_bf16(*ts):
             raise TypeError("g4attn tensors are bfloat16")
 
 
+def _expect(t, shape, name, dtype=None):
+    """Raise unless ``t`` is a CUDA tensor of exactly ``shape`` (and ``dtype``)."""
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}")
+
+
 def _raise(status, where):
     if status != OK:
         raise G4AttnError(status, where)
@@ -155,6 +167,14 @@ def g4attn_norm_rope(x, y, weight, head_dim, rotary_dims, rope_theta, rms_eps=1e
     lib = load()
     _check_bf16(x, y, weight)
     B, S, H, D = x.shape
+    if D != head_dim:
+        raise ValueError(f"x has head_dim {D}, expected {head_dim}")
+    _expect(x, (B, S, H, D), "x")
+    _expect(y, (B, H, cache_cap, D) if cache_cap else (B, S, H, D), "y")
+    _expect(weight, (D,), "weight")
+    _expect(pos0, (B,), "pos0", torch.int32)
+    if cache_cap and not y.is_contiguous():
+        raise ValueError("a cache must be contiguous")
     xs = _bsh_strides(x)
     ys = _I64x3(0, 0, 0) if cache_cap else _bsh_strides(y)
     if max_pos is None:
@@ -189,6 +209,19 @@ def g4attn_prefill(desc, q, k, v, out, w_k=None, lse=None, workspace=None, strea
     lib = load()
     _check_bf16(q, k, v, out, w_k)
     B, S = q.shape[0], q.shape[1]
+    Hq, Hkv, D = desc.num_q_heads, desc.num_kv_heads, desc.head_dim
+    _expect(q, (B, S, Hq, D), "q")
+    _expect(k, (B, S, Hkv, D), "k")
+    _expect(v, (B, S, Hkv, D), "v")
+    _expect(out, (B, S, Hq, D), "out")
+    _expect(w_k, (D,), "w_k")
+    _expect(lse, (B, Hq, S), "lse", torch.float32)
+    _expect(span_lo, (B, S), "span_lo")
+    _expect(span_hi, (B, S), "span_hi")
+    if lse is not None and not lse.is_contiguous():
+        raise ValueError("lse must be contiguous")
+    if v is not None and v.stride() != k.stride():
+        raise ValueError("k and v must have the same strides (one kv_strides argument)")
     need = lib.g4attn_prefill_workspace_bytes(ctypes.byref(desc), B, S)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -201,22 +234,34 @@ def g4attn_prefill(desc, q, k, v, out, w_k=None, lse=None, workspace=None, strea
     return out
 
 
-def g4attn_prefill_chunk(desc, q, k_cache, v_cache, out, pos0, qlen, max_pos, lse=None, workspace=None,
+def g4attn_prefill_chunk(desc, q, k_cache, v_cache, out, pos0, qlen, max_pos=None, lse=None, workspace=None,
                          stream=None, span_lo=None, span_hi=None):
     """Chunked prefill over caches; see g4attn_prefill_chunk in g4attn.h.  Returns ``out``.
 
     ``q``/``out`` [B, S, Hq, D]; ``k_cache``, ``v_cache`` contiguous
     [B, Hkv, cap, D]; ``pos0``, ``qlen`` int32 device tensors [B].
+    ``max_pos`` (the bound of every pos0[b] + qlen[b] - 1) is read from
+    ``pos0`` and ``qlen`` when not given (a device-to-host copy).
     """
     lib = load()
     _check_bf16(q, k_cache, v_cache, out)
-    for t in (pos0, qlen):
-        if t.dtype != torch.int32:
-            raise TypeError("pos0 and qlen must be int32")
+    B, S = q.shape[0], q.shape[1]
+    Hq, Hkv, D = desc.num_q_heads, desc.num_kv_heads, desc.head_dim
+    cap = k_cache.shape[2]
+    _expect(q, (B, S, Hq, D), "q")
+    _expect(out, (B, S, Hq, D), "out")
+    _expect(k_cache, (B, Hkv, cap, D), "k_cache")
+    _expect(v_cache, (B, Hkv, cap, D), "v_cache")
+    _expect(pos0, (B,), "pos0", torch.int32)
+    _expect(qlen, (B,), "qlen", torch.int32)
+    _expect(lse, (B, Hq, S), "lse", torch.float32)
+    _expect(span_lo, (B, S), "span_lo")
+    _expect(span_hi, (B, S), "span_hi")
     for t in (k_cache, v_cache):
         if not t.is_contiguous():
             raise ValueError("caches must be contiguous")
-    B, S = q.shape[0], q.shape[1]
+    if max_pos is None:
+        max_pos = int((pos0.to(torch.int64) + qlen.to(torch.int64)).max().item()) - 1
     need = lib.g4attn_prefill_workspace_bytes(ctypes.byref(desc), B, S)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -250,8 +295,13 @@ def g4attn_decode(desc, q, k_cache, v_cache, kv_len, max_kv_len, out, lse=None, 
             raise ValueError("decode tensors must be contiguous")
     B = q.shape[0]
     cap = k_cache.shape[2]
-    if v_cache.shape != k_cache.shape:
-        raise ValueError("k_cache and v_cache shapes differ")
+    Hq, Hkv, D = desc.num_q_heads, desc.num_kv_heads, desc.head_dim
+    _expect(q, (B, Hq, D), "q")
+    _expect(out, (B, Hq, D), "out")
+    _expect(k_cache, (B, Hkv, cap, D), "k_cache")
+    _expect(v_cache, (B, Hkv, cap, D), "v_cache")
+    _expect(kv_len, (B,), "kv_len", torch.int32)
+    _expect(lse, (B, Hq), "lse", torch.float32)
     need = lib.g4attn_decode_workspace_bytes(ctypes.byref(desc), B, max_kv_len, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
@@ -273,7 +323,14 @@ def g4attn_kv_tied_append(x, w_k, x_cache, r_cache, krot_cache, rope_theta, rms_
     for t in (x_cache, r_cache, krot_cache):
         if not t.is_contiguous():
             raise ValueError("caches must be contiguous")
-    B, S, Hkv, _ = x.shape
+    B, S, Hkv, D = x.shape
+    cap = x_cache.shape[2]
+    _expect(x, (B, S, Hkv, 512), "x")
+    _expect(w_k, (512,), "w_k")
+    _expect(x_cache, (B, Hkv, cap, 512), "x_cache")
+    _expect(r_cache, (B, Hkv, cap), "r_cache")
+    _expect(krot_cache, (B, Hkv, cap, 128), "krot_cache")
+    _expect(pos0, (B,), "pos0", torch.int32)
     if max_pos is None:
         max_pos = S - 1 if pos0 is None else int(pos0.max().item()) + S - 1
     st = lib.g4attn_kv_tied_append(_ptr(x), _ptr(w_k), B, S, Hkv, rotary_dims, rope_theta, rms_eps,
@@ -293,6 +350,16 @@ def g4attn_decode_tied(desc, q, x_cache, r_cache, krot_cache, w_k, kv_len, max_k
         if not t.is_contiguous():
             raise ValueError("decode tensors must be contiguous")
     B = q.shape[0]
+    Hq, Hkv, D = desc.num_q_heads, desc.num_kv_heads, desc.head_dim
+    cap = x_cache.shape[2]
+    _expect(q, (B, Hq, D), "q")
+    _expect(out, (B, Hq, D), "out")
+    _expect(x_cache, (B, Hkv, cap, D), "x_cache")
+    _expect(r_cache, (B, Hkv, cap), "r_cache", torch.float32)
+    _expect(krot_cache, (B, Hkv, cap, 128), "krot_cache")
+    _expect(w_k, (D,), "w_k")
+    _expect(kv_len, (B,), "kv_len", torch.int32)
+    _expect(lse, (B, Hq), "lse", torch.float32)
     need = lib.g4attn_decode_workspace_bytes(ctypes.byref(desc), B, max_kv_len, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
@@ -310,11 +377,3 @@ def g4attn_status_str(status):
 
 def g4attn_version():
     return load().g4attn_version()
-
-
-# ------------------------------------------------------------ host-side logic
-def visible_pairs(S, window):
-    """Visible (row, key) pairs of one head: row i sees min(i+1, w) keys (all i+1 if global)."""
-    if window == 0 or S <= window:
-        return S * (S + 1) // 2
-    return window * (window + 1) // 2 + (S - window) * window

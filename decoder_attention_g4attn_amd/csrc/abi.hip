@@ -242,7 +242,7 @@ g4attn_status g4attn_prefill_chunk(const g4attn_layer_desc* d, const g4attn_bf16
 
   g4attn::PrefillArgs a{};
   a.q = q; a.k = k_cache; a.v = v_cache; a.out = out; a.lse = lse;
-  a.pos0 = pos0; a.qlen = qlen;
+  a.pos0 = pos0; a.qlen = qlen; a.max_pos = max_pos;
   a.span_lo = span_lo; a.span_hi = span_hi;
   a.B = B; a.S = S; a.Hq = d->num_q_heads; a.Hkv = d->num_kv_heads; a.D = d->head_dim;
   a.window = d->window; a.kv_tied = 0;

@@ -90,15 +90,32 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = a.Hq / a.Hkv;
+  RedoCursor redo{(int64_t)a.nsplit * a.Hkv * a.B};
+  for (;;) {
+  int split, g, b;
+  if (REDO) {
+    // the next chunk whose main pass flagged a reference overflow (flag of
+    // chunk L = split + nsplit (g + Hkv b) at dflags[L])
+    const int64_t L = redo.next([&](int64_t c) { return a.dflags[c] != 0; });
+    if (L < 0) return;
+    split = (int)(L % a.nsplit);
+    g = (int)((L / a.nsplit) % a.Hkv);
+    b = (int)(L / ((int64_t)a.nsplit * a.Hkv));
+  } else {
+    split = blockIdx.x;
+    g = blockIdx.y;
+    b = blockIdx.z;
+  }
   const int n = min(max(a.kv_len[b], 0), a.max_len);
   const int r0 = split * a.chunk;
-  if (r0 >= n) return;  // beyond this sequence: the combine never reads it
+  if (r0 >= n) {  // beyond this sequence: the combine never reads it
+    if (!REDO) return;
+    continue;
+  }
   const int r1 = min(r0 + a.chunk, n);
   const int ntile = (r1 - r0 + kRows - 1) / kRows;
   const int64_t blk = ((int64_t)b * a.Hkv + g) * a.nsplit + split;
-  if (REDO && a.dflags[blk] == 0) return;
 
   const int64_t slice = ((int64_t)b * a.Hkv + g) * a.cap * D;
   const uint16_t* kbase = a.kc + slice;
@@ -238,6 +255,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     a.o_part[(ph * a.nsplit + split) * D + d] = O / L;
     if (d == 0) a.lse_part[ph * a.nsplit + split] = (M + __log2f(L)) * kLn2;
   }
+  if (!REDO) return;
+  __syncthreads();  // every wave is done with the LDS before the next chunk reuses it
+  }
 }
 
 // K=V decode over the raw tied projection (the global layer's own cache
@@ -266,15 +286,32 @@ __global__ __launch_bounds__(kWavesT * 64) void decode_tied_kernel(DecodeArgs a)
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = a.Hq / a.Hkv;
+  RedoCursor redo{(int64_t)a.nsplit * a.Hkv * a.B};
+  for (;;) {
+  int split, g, b;
+  if (REDO) {
+    // the next chunk whose main pass flagged a reference overflow (flag of
+    // chunk L = split + nsplit (g + Hkv b) at dflags[L])
+    const int64_t L = redo.next([&](int64_t c) { return a.dflags[c] != 0; });
+    if (L < 0) return;
+    split = (int)(L % a.nsplit);
+    g = (int)((L / a.nsplit) % a.Hkv);
+    b = (int)(L / ((int64_t)a.nsplit * a.Hkv));
+  } else {
+    split = blockIdx.x;
+    g = blockIdx.y;
+    b = blockIdx.z;
+  }
   const int n = min(max(a.kv_len[b], 0), a.max_len);
   const int r0 = split * a.chunk;
-  if (r0 >= n) return;  // beyond this sequence: the combine never reads it
+  if (r0 >= n) {  // beyond this sequence: the combine never reads it
+    if (!REDO) return;
+    continue;
+  }
   const int r1 = min(r0 + a.chunk, n);
   const int ntile = (r1 - r0 + kRows - 1) / kRows;
   const int64_t blk = ((int64_t)b * a.Hkv + g) * a.nsplit + split;
-  if (REDO && a.dflags[blk] == 0) return;
 
   const int64_t srow = ((int64_t)b * a.Hkv + g) * a.cap;   // first cache row of this (b, g)
   const uint16_t* xbase = a.kc + srow * D;
@@ -428,6 +465,9 @@ __global__ __launch_bounds__(kWavesT * 64) void decode_tied_kernel(DecodeArgs a)
     a.o_part[(ph * a.nsplit + split) * D + d] = O / L;
     if (d == 0) a.lse_part[ph * a.nsplit + split] = (M + __log2f(L)) * kLn2;
   }
+  if (!REDO) return;
+  __syncthreads();  // every wave is done with the LDS before the next chunk reuses it
+  }
 }
 
 template <int D>
@@ -455,6 +495,12 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   if (a.lse && threadIdx.x == 0) a.lse[ph] = lse;
 }
 
+// Recompute launch: persistent workgroups that test every chunk's flag.
+dim3 redo_grid(const dim3& gr) {
+  const int64_t n = (int64_t)gr.x * gr.y * gr.z;
+  return dim3((unsigned)(n < 1024 ? n : 1024));
+}
+
 template <int D, bool SAME>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t st) {
   typedef DCfg<D, SAME> C;
@@ -462,7 +508,7 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((decode_split_kernel<D, SAME, false>), grid, dim3(C::WAVES * 64), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_split_kernel<D, SAME, true>), grid, dim3(C::WAVES * 64), 0, st, a);
+  hipLaunchKernelGGL((decode_split_kernel<D, SAME, true>), redo_grid(grid), dim3(C::WAVES * 64), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.Hq, a.B), dim3(256), 0, st, a);
@@ -476,7 +522,7 @@ hipError_t launch_decode_tied(const DecodeArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(decode_tied_kernel<false>, grid, dim3(kWavesT * 64), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_tied_kernel<true>, grid, dim3(kWavesT * 64), 0, st, a);
+  hipLaunchKernelGGL(decode_tied_kernel<true>, redo_grid(grid), dim3(kWavesT * 64), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<512>), dim3(a.Hq, a.B), dim3(256), 0, st, a);

@@ -68,39 +68,49 @@ __device__ __forceinline__ float wave_sum(float v) {
 // Callers therefore order them explicitly: `s_waitcnt vmcnt` (wait_vmem*)
 // before any read of the data, and a workgroup barrier before a buffer is
 // reused.  The instruction has no register results.
+//
+// The LDS destination travels in m0, a register the compiler reserves for
+// itself, so each block saves m0 in a scratch SGPR, sets it, issues the load
+// (which reads m0 when it is issued) and restores it: whatever the compiler
+// keeps in m0 survives every copy.
 __device__ __forceinline__ uint32_t lds_addr(const G4_LDS void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
 }
 __device__ __forceinline__ void g2lds16(const void* gptr, G4_LDS void* lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr(lds_base))
-               : "memory", "m0");
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "v"(gptr), "s"(lds_addr(lds_base))
+      : "memory");
 }
 __device__ __forceinline__ void g2lds4(const void* gptr, G4_LDS void* lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(lds_addr(lds_base))
-               : "memory", "m0");
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "v"(gptr), "s"(lds_addr(lds_base))
+      : "memory");
 }
 
 // The same copies with a wave-uniform 64-bit base in scalar registers plus
 // an unsigned 32-bit per-lane byte offset (the scalar-base form); `lds` is the
 // wave-uniform LDS byte address of lane 0's destination.
 __device__ __forceinline__ void g2lds16s(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
-               "s"(__builtin_amdgcn_readfirstlane(lds))
-               : "memory", "m0");
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds))
+      : "memory");
 }
 __device__ __forceinline__ void g2lds4s(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase),
-               "s"(__builtin_amdgcn_readfirstlane(lds))
-               : "memory", "m0");
-}
-
-// As g2lds16s with the LDS destination formed in m0 as `lds + imm`
-// (`lds` wave-uniform, `imm` a compile-time byte offset).
-template <int IMM>
-__device__ __forceinline__ void g2lds16si(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
-               "s"(__builtin_amdgcn_readfirstlane(lds)), "i"(IMM)
-               : "memory", "m0");
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dword %1, %2\n\ts_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds))
+      : "memory");
 }
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const G4_LDS char* p) {
@@ -123,6 +133,35 @@ __device__ __forceinline__ void wait_vmem() {
   static_assert(N >= 0 && N <= 63, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+
+// Recompute launches: a small grid of persistent workgroups, workgroup w
+// owning candidates L = w, w + grid, w + 2 grid, ... below `ntotal`.  The
+// candidates are tested 64 at a time, one per lane (every wave of the
+// workgroup tests the same 64 and gets the same ballot), so a launch that
+// finds nothing to redo costs one round of flag loads.  next() returns the
+// next candidate whose flagged(L) is true, or -1 when none is left; the
+// result is wave-uniform and equal in every wave, so the caller may run
+// workgroup barriers between calls.
+struct RedoCursor {
+  int64_t ntotal;
+  int64_t k0 = -64;  // first candidate index of the current round
+  uint64_t mk = 0;   // flagged candidates of the round not yet returned
+
+  template <class Flagged>
+  __device__ __forceinline__ int64_t next(Flagged flagged) {
+    for (;;) {
+      if (mk) {
+        const int j = __builtin_ctzll(mk);
+        mk &= mk - 1;
+        return (int64_t)blockIdx.x + (k0 + j) * (int64_t)gridDim.x;
+      }
+      k0 += 64;
+      if ((int64_t)blockIdx.x + k0 * gridDim.x >= ntotal) return -1;
+      const int64_t Lt = (int64_t)blockIdx.x + (k0 + (threadIdx.x & 63)) * (int64_t)gridDim.x;
+      mk = __builtin_amdgcn_ballot_w64(Lt < ntotal && flagged(Lt));
+    }
+  }
+};
 
 }  // namespace g4attn
 
@@ -169,6 +208,7 @@ struct PrefillArgs {
   int* flags;               // [B, Hkv, ntiles, 4] per-wave reference-overflow flags
   const int32_t* pos0;      // NULL, or [B] first query position of each sequence (keys from caches)
   const int32_t* qlen;      // NULL, or [B] valid query rows of each sequence (the rest is padding)
+  int max_pos;              // with pos0: host bound of every key position (rows past it are not computed)
   const int32_t* span_lo;   // NULL, or [B, S] first key of each row's bidirectional span
   const int32_t* span_hi;   // [B, S] its last key (with span_lo)
   uint16_t* out;

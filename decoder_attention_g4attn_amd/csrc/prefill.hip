@@ -93,8 +93,8 @@ struct TileSrc {
   const char* v;      // V row key0
   const char* krot;   // K=V: Krot row key0
   const float* r;     // K=V: key factors from key0
-  uint32_t last_off;  // byte offset of the last in-range key row (key_end-1) from row key0
-  int last;           // its index
+  uint32_t last_off;  // byte offset from row key0 of the row that stands in for rows past key_end-1
+  int last;           // its index within the tile: min(key_end-1-key0, kBN-1)
 };
 
 // key_end: one past the last valid key of sequence b (S, or the chunk's end
@@ -109,7 +109,9 @@ __device__ __forceinline__ TileSrc tile_src(const PrefillArgs& a, int kt, int b,
   const int64_t row0 = ((int64_t)b * a.Hkv + g) * a.S + key0;
   t.krot = TIED ? (const char*)(a.krot + row0 * 128) : nullptr;
   t.r = TIED ? a.r + row0 : nullptr;
-  t.last = key_end - 1 - key0;
+  // Only rows 0..kBN-1 of the tile are copied, so the clamp row never needs
+  // to exceed kBN-1; clamping first keeps last * stride within 32 bits.
+  t.last = min(key_end - 1 - key0, kBN - 1);
   t.last_off = (uint32_t)t.last * (uint32_t)(a.ks[1] * 2);
   return t;
 }
@@ -238,29 +240,37 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const int G = a.Hq / a.Hkv;
   const int ntiles = (int)(((int64_t)a.S * G + kBM - 1) / kBM);
   // Main pass: one workgroup per row tile.  Recompute pass: a small grid of
-  // persistent workgroups walks every row tile and redoes the flagged ones
-  // (most launches find none, and a full grid of early exits costs ~30 us).
-  const int ntotal = ntiles * a.Hkv * a.B;
-  for (int L = REDO ? (int)blockIdx.x : 0;; L += (int)gridDim.x) {
+  // persistent workgroups tests every row tile's flags in parallel and redoes
+  // the flagged ones (most launches find none).
+  RedoCursor redo{(int64_t)ntiles * a.Hkv * a.B};
+  for (;;) {
     int b, g, tile;
     if (REDO) {
-      if (L >= ntotal) return;
-      tile = L % ntiles;
-      g = (L / ntiles) % a.Hkv;
-      b = L / (ntiles * a.Hkv);
-      const int* fl = a.flags + (((int64_t)b * a.Hkv + g) * ntiles + tile) * kWaves;
-      int any = 0;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) any |= fl[w];
-      if (any == 0) continue;  // uniform: every thread reads the same flags
+      // the next row tile whose main pass flagged a reference overflow (the
+      // flags of tile L = tile + ntiles (g + Hkv b) sit at flags[L * waves])
+      const int64_t L = redo.next([&](int64_t c) {
+        const u32x4 f = *(const u32x4*)(a.flags + c * kWaves);
+        return (f[0] | f[1] | f[2] | f[3]) != 0u;
+      });
+      if (L < 0) return;
+      tile = (int)(L % ntiles);
+      g = (int)((L / ntiles) % a.Hkv);
+      b = (int)(L / ((int64_t)ntiles * a.Hkv));
     } else {
       wg_map(ntiles, a.Hkv, b, g, tile);
     }
 
     // Rows t < n of this sequence are positions P + t (P = 0, n = S unless
     // the keys come from a cache: chunked prefill, padded batches).
-    const int P = EXT && a.pos0 ? a.pos0[b] : 0;
-    const int n = EXT && a.qlen ? min(a.qlen[b], a.S) : a.S;
+    // Device-side values are clamped: a sequence with pos0 < 0 has no rows,
+    // and rows past the host's bound max_pos are not computed, so no key
+    // past the cache is ever read.
+    int P = 0, n = a.S;
+    if (EXT && a.pos0) {
+      P = a.pos0[b];
+      n = a.qlen ? min(a.qlen[b], a.S) : a.S;
+      n = P < 0 ? 0 : max(0, min(n, a.max_pos + 1 - P));
+    }
     const int key_end = P + n;  // keys [0, key_end) exist
     const int64_t F0 = (int64_t)tile * kBM;
     const int64_t Flast = min(F0 + kBM - 1, (int64_t)a.S * G - 1);
@@ -278,7 +288,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     // the lowest and its last valid row the highest.
     const bool spans = EXT && a.span_lo != nullptr;
     const int64_t srow = (int64_t)b * a.S;
-    const int kt_lo = min(a.window ? max(0, tq0 - a.window + 1) : 0, spans ? a.span_lo[srow + tr0] : tq0) / kBN;
+    const int kt_lo = max(0, min(a.window ? tq0 - a.window + 1 : 0, spans ? a.span_lo[srow + tr0] : tq0)) / kBN;
     const int kt_hi = min(max(tq1, spans ? a.span_hi[srow + tr1] : tq1), key_end - 1) / kBN;
     int* wg_flags = a.flags + (((int64_t)b * a.Hkv + g) * ntiles + tile) * kWaves;
     if (EXT && tq0 > tq1) {  // only padding rows: nothing to compute (uniform)
@@ -679,29 +689,37 @@ void prefill_d256_kernel(PrefillArgs a) {
   const int G = a.Hq / a.Hkv;
   const int ntiles = (int)(((int64_t)a.S * G + BM - 1) / BM);
   // Main pass: one workgroup per row tile.  Recompute pass: a small grid of
-  // persistent workgroups walks every row tile and redoes the flagged ones
-  // (most launches find none, and a full grid of early exits costs ~30 us).
-  const int ntotal = ntiles * a.Hkv * a.B;
-  for (int L = REDO ? (int)blockIdx.x : 0;; L += (int)gridDim.x) {
+  // persistent workgroups tests every row tile's flags in parallel and redoes
+  // the flagged ones (most launches find none).
+  RedoCursor redo{(int64_t)ntiles * a.Hkv * a.B};
+  for (;;) {
     int b, g, tile;
     if (REDO) {
-      if (L >= ntotal) return;
-      tile = L % ntiles;
-      g = (L / ntiles) % a.Hkv;
-      b = L / (ntiles * a.Hkv);
-      const int* fl = a.flags + (((int64_t)b * a.Hkv + g) * ntiles + tile) * NW;
-      int any = 0;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) any |= fl[w];
-      if (any == 0) continue;  // uniform: every thread reads the same flags
+      // the next row tile whose main pass flagged a reference overflow (the
+      // flags of tile L = tile + ntiles (g + Hkv b) sit at flags[L * waves])
+      const int64_t L = redo.next([&](int64_t c) {
+        const u32x4 f = *(const u32x4*)(a.flags + c * NW);
+        return (f[0] | f[1] | f[2] | f[3]) != 0u;
+      });
+      if (L < 0) return;
+      tile = (int)(L % ntiles);
+      g = (int)((L / ntiles) % a.Hkv);
+      b = (int)(L / ((int64_t)ntiles * a.Hkv));
     } else {
       wg_map(ntiles, a.Hkv, b, g, tile);
     }
 
     // Rows t < n of this sequence are positions P + t (P = 0, n = S unless
     // the keys come from a cache: chunked prefill, padded batches).
-    const int P = EXT && a.pos0 ? a.pos0[b] : 0;
-    const int n = EXT && a.qlen ? min(a.qlen[b], a.S) : a.S;
+    // Device-side values are clamped: a sequence with pos0 < 0 has no rows,
+    // and rows past the host's bound max_pos are not computed, so no key
+    // past the cache is ever read.
+    int P = 0, n = a.S;
+    if (EXT && a.pos0) {
+      P = a.pos0[b];
+      n = a.qlen ? min(a.qlen[b], a.S) : a.S;
+      n = P < 0 ? 0 : max(0, min(n, a.max_pos + 1 - P));
+    }
     const int key_end = P + n;  // keys [0, key_end) exist
     const int64_t F0 = (int64_t)tile * BM;
     const int64_t Flast = min(F0 + BM - 1, (int64_t)a.S * G - 1);
@@ -719,7 +737,7 @@ void prefill_d256_kernel(PrefillArgs a) {
     // the lowest and its last valid row the highest.
     const bool spans = EXT && a.span_lo != nullptr;
     const int64_t srow = (int64_t)b * a.S;
-    const int kt_lo = min(a.window ? max(0, tq0 - a.window + 1) : 0, spans ? a.span_lo[srow + tr0] : tq0) / kBN;
+    const int kt_lo = max(0, min(a.window ? tq0 - a.window + 1 : 0, spans ? a.span_lo[srow + tr0] : tq0)) / kBN;
     const int kt_hi = min(max(tq1, spans ? a.span_hi[srow + tr1] : tq1), key_end - 1) / kBN;
     int* wg_flags = a.flags + (((int64_t)b * a.Hkv + g) * ntiles + tile) * NW;
     if (EXT && tq0 > tq1) {  // only padding rows: nothing to compute (uniform)

@@ -215,28 +215,29 @@ def decode_attention(q, k_cache, v_cache, n, scale, heads=None, batch=None):
     return out, lse
 
 
-def visible_count(S, window):
-    """Number of keys each prefill row sees, by enumeration of the mask."""
-    i = np.arange(S)[:, None]
+def visible_count(S, window, span_lo=None, span_hi=None, block=512):
+    """Number of keys each prefill row sees, by enumeration of the mask.
+
+    Every (row, key) pair of the ``S x S`` grid is tested with
+    :func:`visible` (and, with spans, the span rule of :func:`mask_spans`),
+    a block of rows at a time so that long sequences stay within memory.
+    """
+    counts = np.zeros(S, dtype=np.int64)
     j = np.arange(S)[None, :]
-    return visible(i, j, window).sum(axis=1)
+    for r0 in range(0, S, block):
+        i = np.arange(r0, min(S, r0 + block))[:, None]
+        m = visible(i, j, window)
+        if span_lo is not None:
+            lo = np.asarray(span_lo)[r0:r0 + block][:, None]
+            hi = np.asarray(span_hi)[r0:r0 + block][:, None]
+            m = m | ((j >= lo) & (j <= hi))
+        counts[r0:r0 + block] = m.sum(axis=1)
+    return counts
 
 
 def visible_pairs(S, window):
-    """Total visible (row, key) pairs of one head, by the count per row."""
-    return int(visible_count(S, window).sum()) if S <= 4096 else _pairs_closed(S, window)
-
-
-def _pairs_closed(S, window):
-    # Counting rows of the mask in closed form: row i sees min(i+1, w) keys
-    # (all i+1 for a global layer).  Used for sizes whose S x S mask would
-    # not fit in memory; equality with the enumeration is tested.
-    if window == 0:
-        return S * (S + 1) // 2
-    w = window
-    if S <= w:
-        return S * (S + 1) // 2
-    return w * (w + 1) // 2 + (S - w) * w
+    """Total visible (row, key) pairs of one head: the per-row counts summed."""
+    return int(visible_count(S, window).sum())
 
 
 def ring_positions(n, window):

@@ -197,9 +197,3 @@ def test_norm_rope_validation():
     # ring mode needs a cache and is a flag
     assert call(ring=1) == g4.ERR_SHAPE
     assert call(cap=64, ring=2) == g4.ERR_SHAPE
-
-
-def test_visible_pairs_host_logic_matches_oracle():
-    from oracle import attention as at
-    for S, w in [(1024, 512), (8192, 0), (16384, 1024), (32768, 0), (5, 8), (100, 1)]:
-        assert g4.visible_pairs(S, w) == at._pairs_closed(S, w)

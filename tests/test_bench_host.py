@@ -19,3 +19,8 @@ def test_image_spans_layout():
     lo, hi = gen.image_spans(12, [(2, 3), (9, 3)])
     assert lo.tolist() == [0, 1, 2, 2, 2, 5, 6, 7, 8, 9, 9, 9]
     assert hi.tolist() == [0, 1, 4, 4, 4, 5, 6, 7, 8, 11, 11, 11]
+
+
+@pytest.mark.parametrize("S,w", [(1024, 512), (8192, 0), (16384, 1024), (5, 8), (100, 1), (3000, 700)])
+def test_visible_pair_count_matches_the_mask(S, w):
+    assert bench.visible_pairs(S, w) == oat.visible_pairs(S, w)

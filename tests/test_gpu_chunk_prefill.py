@@ -113,3 +113,29 @@ def test_prefill_chunk_reference_overflow_redo(gpu_lib, D, w):
     ro, rl = oat.attention_masked(qf.numpy(), kf, vf, 1.0, m)
     assert_parity(f64(out), ro[:, P:], f"chunk redo D={D} w={w}")
     np.testing.assert_allclose(lse.cpu().numpy(), rl[:, :, P:], rtol=1e-4, atol=2e-3)
+
+
+@pytest.mark.parametrize("D,w", [(256, 64), (512, 0)])
+def test_prefill_chunk_padded_batch_equals_single_bit_exact(gpu_lib, D, w):
+    """A padded batch of chunks equals each sequence's chunk computed alone, bit for bit
+    (gemma4-pt-claude README, "Tests": batched rows match each prompt on its own)."""
+    g4 = gpu_lib
+    total = [300, 150, 97]
+    pos0 = [220, 100, 17]
+    qlen = [80, 50, 80]
+    B, S, cap, Hq, Hkv = 3, 80, 320, 8, 2
+    kc, vc = _caches(B, Hkv, cap, D, total, 140)
+    q = _bf((B, S, Hq, D), 150)
+    desc = g4.layer_desc(Hq, Hkv, D, window=w, rotary_dims=D)
+    out = torch.full((B, S, Hq, D), SENTINEL, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    lse = torch.zeros((B, Hq, S), dtype=torch.float32, device=DEV)
+    g4.g4attn_prefill_chunk(desc, q, kc, vc, out, torch.tensor(pos0, dtype=torch.int32, device=DEV),
+                            torch.tensor(qlen, dtype=torch.int32, device=DEV), 299, lse=lse)
+    for b in range(B):
+        o1 = torch.full((1, S, Hq, D), SENTINEL, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+        l1 = torch.zeros((1, Hq, S), dtype=torch.float32, device=DEV)
+        g4.g4attn_prefill_chunk(desc, q[b:b + 1], kc[b:b + 1], vc[b:b + 1], o1,
+                                torch.tensor([pos0[b]], dtype=torch.int32, device=DEV),
+                                torch.tensor([qlen[b]], dtype=torch.int32, device=DEV), 299, lse=l1)
+        assert torch.equal(out[b:b + 1].view(torch.int16), o1.view(torch.int16)), f"sequence {b}"
+        assert torch.equal(lse[b:b + 1, :, :qlen[b]], l1[:, :, :qlen[b]]), f"sequence {b} lse"

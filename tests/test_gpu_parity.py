@@ -354,3 +354,44 @@ def test_prefill_random_configs_vs_oracle(gpu_lib, B, S, Hq, Hkv, D, w):
     ro, rl = oat.attention_band(f64(q), f64(k), f64(v), desc.scale, w)
     assert_parity(f64(out), ro, f"random B={B} S={S} Hq={Hq} Hkv={Hkv} D={D} w={w}")
     np.testing.assert_allclose(lse.cpu().numpy(), rl, rtol=0, atol=2e-3)
+
+
+# ------------------------------------------------------------------ batching
+@pytest.mark.parametrize("D,w,kv_tied", [(256, 64, False), (512, 0, False), (512, 0, True), (256, 0, False)])
+def test_prefill_batched_equals_single_bit_exact(gpu_lib, D, w, kv_tied):
+    """Batched rows equal each sequence computed on its own, bit for bit
+    (gemma4-pt-claude README, "Tests": batched rows match single prompts):
+    no part of a sequence's computation depends on the batch around it."""
+    g4 = gpu_lib
+    B, S, Hq, Hkv = 3, 333, 16, 2
+    q, k, v = _prefill_inputs(B, S, Hq, Hkv, D, seed=111)
+    wk = _w(D, 112)
+    desc = g4.layer_desc(Hq, Hkv, D, window=w, k_eq_v=kv_tied, rotary_dims=128 if kv_tied else D)
+    vv = None if kv_tied else v
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=DEV)
+    g4.g4attn_prefill(desc, q, k, vv, out, w_k=wk if kv_tied else None, lse=lse)
+    for b in range(B):
+        o1 = torch.empty_like(q[b:b + 1])
+        l1 = torch.empty((1, Hq, S), dtype=torch.float32, device=DEV)
+        g4.g4attn_prefill(desc, q[b:b + 1], k[b:b + 1], None if kv_tied else v[b:b + 1], o1,
+                          w_k=wk if kv_tied else None, lse=l1)
+        assert torch.equal(out[b:b + 1], o1), f"sequence {b}"
+        assert torch.equal(lse[b:b + 1], l1), f"sequence {b} lse"
+
+
+def test_decode_batched_equals_single_bit_exact(gpu_lib):
+    """A decode batch equals each sequence decoded alone when the split
+    partition is the same (explicit split count and length bound)."""
+    g4 = gpu_lib
+    lens = [700, 1, 2049, 1500]
+    for same in (True, False):
+        q, kc, vc, out, lse, desc = _decode_case(g4, len(lens), 16, 2, 512, lens, 2100, same, 3)
+        for b, n in enumerate(lens):
+            o1 = torch.empty_like(q[b:b + 1])
+            l1 = torch.empty((1, 16), dtype=torch.float32, device=DEV)
+            kl = torch.tensor([n], dtype=torch.int32, device=DEV)
+            g4.g4attn_decode(desc, q[b:b + 1], kc[b:b + 1], kc[b:b + 1] if same else vc[b:b + 1], kl, max(lens),
+                             o1, lse=l1, num_splits=3)
+            assert torch.equal(out[b:b + 1], o1), f"same={same} sequence {b}"
+            assert torch.equal(lse[b:b + 1], l1), f"same={same} sequence {b} lse"

@@ -84,17 +84,35 @@ def test_visible_count_closed_form(S, w):
     i = np.arange(S)
     expect = i + 1 if w == 0 else np.minimum(i + 1, w)
     np.testing.assert_array_equal(cnt, expect)
-    assert int(cnt.sum()) == at._pairs_closed(S, w)
+    # closed form of the total: w(w+1)/2 + (S-w)w past the window, else S(S+1)/2
+    total = S * (S + 1) // 2 if (w == 0 or S <= w) else w * (w + 1) // 2 + (S - w) * w
+    assert at.visible_pairs(S, w) == total
     if S <= 64:
         np.testing.assert_array_equal(at.mask_bruteforce(S, w).sum(1), expect)
 
 
 def test_workload_pair_counts():
-    # visible pairs per head at the workload shapes, from the closed form
-    assert at._pairs_closed(1024, 512) == 393472
-    assert at._pairs_closed(8192, 0) == 33558528
-    assert at._pairs_closed(16384, 1024) == 16253440
-    assert at._pairs_closed(32768, 0) == 536887296
+    # visible pairs per head at the workload shapes (enumerated mask) against
+    # the hand-computed closed forms: 512*513/2 + 512*512, 8192*8193/2,
+    # 1024*1025/2 + 15360*1024, 32768*32769/2
+    assert at.visible_pairs(1024, 512) == 393472
+    assert at.visible_pairs(8192, 0) == 33558528
+    assert at.visible_pairs(16384, 1024) == 16253440
+    assert at.visible_pairs(32768, 0) == 536887296
+
+
+@pytest.mark.parametrize("S,w,images", [(40, 8, [(3, 5), (20, 12)]), (64, 0, [(0, 10), (30, 34)]),
+                                        (300, 64, [(0, 20), (40, 150), (250, 50)])])
+def test_visible_count_with_spans_matches_the_mask(S, w, images):
+    lo, hi = at.span_rows(S, images)
+    cnt = at.visible_count(S, w, lo, hi, block=7)
+    np.testing.assert_array_equal(cnt, at.mask_spans(S, w, lo, hi).sum(axis=1))
+    if S <= 64:   # and the element-by-element mask with the span rule written out
+        m = at.mask_bruteforce(S, w)
+        for i in range(S):
+            for j in range(S):
+                m[i, j] |= bool(lo[i] <= j <= hi[i])
+        np.testing.assert_array_equal(cnt, m.sum(axis=1))
 
 
 def test_window_one_gives_v_and_short_sequences_equal_global():

@@ -36,7 +36,20 @@ def test_rmsnorm_closed_forms():
     # scale invariance when eps = 0
     np.testing.assert_allclose(nr.rms_norm(7.5 * x, None, eps=0.0), nr.rms_norm(x, None, eps=0.0),
                                rtol=1e-13)
-    np.testing.assert_allclose(nr.inv_rms(x), 1.0 / np.sqrt(ms + nr.RMS_EPS), rtol=1e-15)
+
+
+@pytest.mark.parametrize("D,scale", [(512, 1.0), (512, 40.0), (256, 0.01)])
+def test_inv_rms_matches_torch_library(D, scale):
+    """inv_rms is the factor torch's rms_norm applies: rms_norm(x) / x, element by
+    element (a library routine, not the oracle's own formula)."""
+    x = _x(4, 33, D) * scale
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (D,), None, eps=nr.RMS_EPS).numpy()
+    r = nr.inv_rms(x)
+    assert r.shape == x.shape[:-1]
+    np.testing.assert_allclose(r[..., None] * x, ref, rtol=1e-13, atol=1e-13 * scale)
+    np.testing.assert_allclose(ref[..., 5] / x[..., 5], r, rtol=1e-12)
+    # and the factor rescales the weightless norm of the oracle itself
+    np.testing.assert_allclose(r[..., None] * x, nr.rms_norm(x, None), rtol=1e-14)
 
 
 # ---------------------------------------------------------------- RoPE
