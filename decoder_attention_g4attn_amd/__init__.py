@@ -24,7 +24,8 @@ LIB_PATH = os.path.join(_HERE, "libg4attn.so")
 OK, ERR_NULL, ERR_SHAPE, ERR_LAYOUT, ERR_UNSUPPORTED, ERR_CACHE_OVERFLOW, ERR_WORKSPACE, ERR_HIP = range(8)
 
 EXPORTED = ("g4attn_norm_rope", "g4attn_prefill_workspace_bytes", "g4attn_prefill", "g4attn_prefill_chunk",
-            "g4attn_decode_workspace_bytes", "g4attn_decode", "g4attn_kv_tied_append", "g4attn_decode_tied",
+            "g4attn_decode_workspace_bytes", "g4attn_decode", "g4attn_decode_noalloc", "g4attn_kv_tied_append",
+            "g4attn_decode_tied",
             "g4attn_status_str",
             "g4attn_last_hip_error", "g4attn_version")
 
@@ -97,6 +98,9 @@ def load(path=None):
     lib.g4attn_decode.argtypes = [ctypes.POINTER(LayerDesc), _P, _P, _P, _P, ctypes.c_int32,
                                   ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int32, _P,
                                   ctypes.c_size_t, _P]
+    lib.g4attn_decode_noalloc.restype = ctypes.c_int
+    lib.g4attn_decode_noalloc.argtypes = [ctypes.POINTER(LayerDesc), _P, _P, _P, _P, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int32, _P]
     lib.g4attn_kv_tied_append.restype = ctypes.c_int
     lib.g4attn_kv_tied_append.argtypes = [_P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                           ctypes.c_float, ctypes.c_float, _P, _P, ctypes.c_int32, _P, _P, _P,
@@ -310,6 +314,30 @@ def g4attn_decode(desc, q, k_cache, v_cache, kv_len, max_kv_len, out, lse=None, 
                            B, max_kv_len, cap, _ptr(out), _ptr(lse), num_splits, _ptr(workspace),
                            wbytes, _stream(stream))
     _raise(st, "g4attn_decode")
+    return out
+
+
+def g4attn_decode_noalloc(desc, q, k_cache, v_cache, kv_len, max_kv_len, out, lse=None, num_splits=0,
+                          stream=None):
+    """g4attn_decode without a workspace (the library's own per-GPU scratch
+    array); see g4attn_decode_noalloc in g4attn.h.  Allocates nothing.  Returns ``out``."""
+    lib = load()
+    _check_bf16(q, k_cache, v_cache, out)
+    for t in (q, k_cache, v_cache, out):
+        if not t.is_contiguous():
+            raise ValueError("decode tensors must be contiguous")
+    B = q.shape[0]
+    cap = k_cache.shape[2]
+    Hq, Hkv, D = desc.num_q_heads, desc.num_kv_heads, desc.head_dim
+    _expect(q, (B, Hq, D), "q")
+    _expect(out, (B, Hq, D), "out")
+    _expect(k_cache, (B, Hkv, cap, D), "k_cache")
+    _expect(v_cache, (B, Hkv, cap, D), "v_cache")
+    _expect(kv_len, (B,), "kv_len", torch.int32)
+    _expect(lse, (B, Hq), "lse", torch.float32)
+    st = lib.g4attn_decode_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_len),
+                                   B, max_kv_len, cap, _ptr(out), _ptr(lse), num_splits, _stream(stream))
+    _raise(st, "g4attn_decode_noalloc")
     return out
 
 

@@ -67,7 +67,81 @@ int64_t decode_chunk(const g4attn_layer_desc* d, int32_t B, int32_t max_kv_len, 
   return c;
 }
 
+// Cache rows a decode reads at most: sliding layers keep the last `window`
+// positions in a ring of that many slots, so min(kv_len, window) of them.
+int32_t decode_rows(const g4attn_layer_desc* d, int32_t max_kv_len) {
+  return d->window > 0 ? (max_kv_len < d->window ? max_kv_len : d->window) : max_kv_len;
+}
+
 }  // namespace
+
+namespace g4attn {
+
+g4attn_status decode_validate(const g4attn_layer_desc* d, const g4attn_bf16* q, const g4attn_bf16* k_cache,
+                              const g4attn_bf16* v_cache, const int32_t* kv_len, int32_t B, int32_t max_kv_len,
+                              int32_t cache_cap, const g4attn_bf16* out, const float* lse, int32_t num_splits) {
+  g4attn_status st = desc_check(d);
+  if (st != G4ATTN_OK) return st;
+  if (!q || !k_cache || !v_cache || !kv_len || !out) return G4ATTN_ERR_NULL;
+  if (d->num_q_heads / d->num_kv_heads > 16) return G4ATTN_ERR_UNSUPPORTED;
+  if (B < 1 || B > 65535 || max_kv_len < 1 || cache_cap < 1 || num_splits < 0) return G4ATTN_ERR_SHAPE;
+  // sliding layer: the cache is a ring of exactly `window` slots
+  if (d->window != 0 && cache_cap != d->window) return G4ATTN_ERR_SHAPE;
+  if (d->window == 0 && max_kv_len > cache_cap) return G4ATTN_ERR_CACHE_OVERFLOW;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return G4ATTN_ERR_LAYOUT;
+  const int32_t rows = decode_rows(d, max_kv_len);
+  const int64_t c = decode_chunk(d, B, rows, num_splits);
+  if (((int64_t)rows + c - 1) / c > 65535) return G4ATTN_ERR_SHAPE;
+  return G4ATTN_OK;
+}
+
+int32_t decode_fit_splits(const g4attn_layer_desc* d, int32_t B, int32_t max_kv_len, int32_t num_splits,
+                          size_t max_bytes) {
+  if (g4attn_decode_workspace_bytes(d, B, max_kv_len, num_splits) <= max_bytes) return num_splits;
+  if (num_splits > 0) return -1;
+  // the automatic count does not fit: the largest explicit count below it that does
+  const int32_t rows = decode_rows(d, max_kv_len);
+  const int64_t c = decode_chunk(d, B, rows, 0);
+  for (int64_t ns = ((int64_t)rows + c - 1) / c - 1; ns >= 1; --ns)
+    if (g4attn_decode_workspace_bytes(d, B, max_kv_len, (int32_t)ns) <= max_bytes) return (int32_t)ns;
+  return -1;
+}
+
+g4attn_status decode_run(const g4attn_layer_desc* d, const g4attn_bf16* q, const g4attn_bf16* k_cache,
+                         const g4attn_bf16* v_cache, const int32_t* kv_len, int32_t B, int32_t max_kv_len,
+                         int32_t cache_cap, g4attn_bf16* out, float* lse, int32_t num_splits, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  const g4attn_status st =
+      decode_validate(d, q, k_cache, v_cache, kv_len, B, max_kv_len, cache_cap, out, lse, num_splits);
+  if (st != G4ATTN_OK) return st;
+  const int32_t rows = decode_rows(d, max_kv_len);
+  const int64_t c = decode_chunk(d, B, rows, num_splits);
+  const int64_t ns = ((int64_t)rows + c - 1) / c;
+  const size_t need = g4attn_decode_workspace_bytes(d, B, max_kv_len, num_splits);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return G4ATTN_ERR_WORKSPACE;
+
+  const size_t ph = (size_t)B * d->num_q_heads;
+  DecodeArgs a{};
+  a.q = q; a.kc = k_cache; a.vc = v_cache; a.kv_len = kv_len; a.out = out; a.lse = lse;
+  char* wsp = (char*)workspace;
+  a.o_part = (float*)wsp;
+  wsp += align256(ph * ns * d->head_dim * sizeof(float));
+  a.lse_part = (float*)wsp;
+  wsp += align256(ph * ns * sizeof(float));
+  a.dmax = (float*)wsp;
+  wsp += align256(ph * ns * sizeof(float));
+  a.dflags = (int*)wsp;
+  a.B = B; a.Hq = d->num_q_heads; a.Hkv = d->num_kv_heads; a.D = d->head_dim; a.cap = cache_cap;
+  a.nsplit = (int)ns; a.chunk = (int)c; a.max_len = rows;  // kv_len is clamped to rows in the kernel
+  a.scale_log2 = d->scale * kLog2e;
+  return hip_status(launch_decode(a, stream));
+}
+
+g4attn_status status_of_hip(hipError_t e) { return hip_status(e); }
+
+}  // namespace g4attn
 
 extern "C" {
 
@@ -259,12 +333,6 @@ g4attn_status g4attn_prefill_chunk(const g4attn_layer_desc* d, const g4attn_bf16
   return hip_status(g4attn::launch_prefill(a, (hipStream_t)stream));
 }
 
-// Cache rows a decode reads at most: sliding layers keep the last `window`
-// positions in a ring of that many slots, so min(kv_len, window) of them.
-static int32_t decode_rows(const g4attn_layer_desc* d, int32_t max_kv_len) {
-  return d->window > 0 ? (max_kv_len < d->window ? max_kv_len : d->window) : max_kv_len;
-}
-
 size_t g4attn_decode_workspace_bytes(const g4attn_layer_desc* d, int32_t B, int32_t max_kv_len,
                                      int32_t num_splits) {
   if (!d || B < 1 || max_kv_len < 1 || num_splits < 0 || d->num_kv_heads < 1 || d->num_q_heads < 1 ||
@@ -284,39 +352,8 @@ g4attn_status g4attn_decode(const g4attn_layer_desc* d, const g4attn_bf16* q,
                             const int32_t* kv_len, int32_t B, int32_t max_kv_len,
                             int32_t cache_cap, g4attn_bf16* out, float* lse, int32_t num_splits,
                             void* workspace, size_t workspace_bytes, void* stream) {
-  g4attn_status st = desc_check(d);
-  if (st != G4ATTN_OK) return st;
-  if (!q || !k_cache || !v_cache || !kv_len || !out) return G4ATTN_ERR_NULL;
-  if (d->num_q_heads / d->num_kv_heads > 16) return G4ATTN_ERR_UNSUPPORTED;
-  if (B < 1 || B > 65535 || max_kv_len < 1 || cache_cap < 1 || num_splits < 0) return G4ATTN_ERR_SHAPE;
-  // sliding layer: the cache is a ring of exactly `window` slots
-  if (d->window != 0 && cache_cap != d->window) return G4ATTN_ERR_SHAPE;
-  if (d->window == 0 && max_kv_len > cache_cap) return G4ATTN_ERR_CACHE_OVERFLOW;
-  const int32_t rows = decode_rows(d, max_kv_len);
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
-      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
-    return G4ATTN_ERR_LAYOUT;
-  const int64_t c = decode_chunk(d, B, rows, num_splits);
-  const int64_t ns = ((int64_t)rows + c - 1) / c;
-  if (ns > 65535) return G4ATTN_ERR_SHAPE;
-  const size_t need = g4attn_decode_workspace_bytes(d, B, max_kv_len, num_splits);
-  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return G4ATTN_ERR_WORKSPACE;
-
-  const size_t ph = (size_t)B * d->num_q_heads;
-  g4attn::DecodeArgs a{};
-  a.q = q; a.kc = k_cache; a.vc = v_cache; a.kv_len = kv_len; a.out = out; a.lse = lse;
-  char* wsp = (char*)workspace;
-  a.o_part = (float*)wsp;
-  wsp += align256(ph * ns * d->head_dim * sizeof(float));
-  a.lse_part = (float*)wsp;
-  wsp += align256(ph * ns * sizeof(float));
-  a.dmax = (float*)wsp;
-  wsp += align256(ph * ns * sizeof(float));
-  a.dflags = (int*)wsp;
-  a.B = B; a.Hq = d->num_q_heads; a.Hkv = d->num_kv_heads; a.D = d->head_dim; a.cap = cache_cap;
-  a.nsplit = (int)ns; a.chunk = (int)c; a.max_len = rows;  // kv_len is clamped to rows in the kernel
-  a.scale_log2 = d->scale * g4attn::kLog2e;
-  return hip_status(g4attn::launch_decode(a, (hipStream_t)stream));
+  return g4attn::decode_run(d, q, k_cache, v_cache, kv_len, B, max_kv_len, cache_cap, out, lse, num_splits,
+                            workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 g4attn_status g4attn_kv_tied_append(const g4attn_bf16* x, const g4attn_bf16* w_k, int32_t B, int32_t S,

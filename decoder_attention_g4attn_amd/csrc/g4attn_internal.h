@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/g4attn.h"
+
 namespace g4attn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -242,5 +244,19 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_tied(const DecodeArgs& a, hipStream_t st);
+
+// Decode entry shared by g4attn_decode and g4attn_decode_noalloc (abi.hip):
+// host validation of everything but the workspace, the split count whose
+// workspace fits max_bytes (-1 if none), and validation + launch.
+g4attn_status decode_validate(const g4attn_layer_desc* d, const g4attn_bf16* q, const g4attn_bf16* k_cache,
+                              const g4attn_bf16* v_cache, const int32_t* kv_len, int32_t B, int32_t max_kv_len,
+                              int32_t cache_cap, const g4attn_bf16* out, const float* lse, int32_t num_splits);
+int32_t decode_fit_splits(const g4attn_layer_desc* d, int32_t B, int32_t max_kv_len, int32_t num_splits,
+                          size_t max_bytes);
+g4attn_status decode_run(const g4attn_layer_desc* d, const g4attn_bf16* q, const g4attn_bf16* k_cache,
+                         const g4attn_bf16* v_cache, const int32_t* kv_len, int32_t B, int32_t max_kv_len,
+                         int32_t cache_cap, g4attn_bf16* out, float* lse, int32_t num_splits, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+g4attn_status status_of_hip(hipError_t e);
 
 }  // namespace g4attn

@@ -10,6 +10,7 @@
  *                       caches (chunked prefill, padded batches);
  *   g4attn_decode     - one new query token per sequence over a KV cache
  *                       (split-KV plus a log-sum-exp combine);
+ *   g4attn_decode_noalloc - the same without a workspace argument;
  *   g4attn_kv_tied_append, g4attn_decode_tied - a K=V global layer's cache
  *                       of its raw projection, and decode over it.
  *
@@ -30,7 +31,8 @@
  *   batch, sequence and head strides are given in elements.  Base pointers
  *   and strides must keep every row 16-byte aligned.
  * - Thread-safe: the library keeps no state apart from a thread-local copy
- *   of the last HIP error code.
+ *   of the last HIP error code, and the per-GPU scratch array of
+ *   g4attn_decode_noalloc.
  *
  * Source pages: "Gemma 4" (Keras port documentation), "gemma4-pt-claude"
  * (PyTorch port README) and the vinija.ai "Gemma 4" primer.
@@ -260,6 +262,30 @@ g4attn_status g4attn_decode(const g4attn_layer_desc* desc, const g4attn_bf16* q,
                             const int32_t* kv_len, int32_t B, int32_t max_kv_len,
                             int32_t cache_cap, g4attn_bf16* out, float* lse, int32_t num_splits,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * g4attn_decode for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops and hosts that forbid allocation.
+ * Same arguments, semantics and errors as g4attn_decode, without the
+ * workspace: the call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine).  Its scratch is a 32 MiB device array inside the library,
+ * one per GPU, set up on the first call on that GPU and held until the
+ * process ends.
+ *   num_splits 0: the automatic split count if its partial results fit the
+ *              32 MiB (B * Hq * splits * (4 * head_dim + 8) bytes plus
+ *              alignment), else the largest smaller count that fits;
+ *              > 0: as in g4attn_decode if it fits.
+ *   Sizes that do not fit even as one split (B * Hq * head_dim * 4 bytes
+ *   near or above 32 MiB), or an explicit count that does not fit, return
+ *   G4ATTN_ERR_WORKSPACE with nothing launched.
+ * Every call on one GPU uses the same scratch array: calls that overlap on
+ * one GPU (concurrent streams or host threads) race and must be serialised
+ * by the caller.
+ */
+g4attn_status g4attn_decode_noalloc(const g4attn_layer_desc* desc, const g4attn_bf16* q,
+                                    const g4attn_bf16* k_cache, const g4attn_bf16* v_cache,
+                                    const int32_t* kv_len, int32_t B, int32_t max_kv_len, int32_t cache_cap,
+                                    g4attn_bf16* out, float* lse, int32_t num_splits, void* stream);
 
 /*
  * Append rows to a K=V global layer's own cache: the raw tied projection X

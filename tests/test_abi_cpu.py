@@ -197,3 +197,23 @@ def test_norm_rope_validation():
     # ring mode needs a cache and is a flag
     assert call(ring=1) == g4.ERR_SHAPE
     assert call(cap=64, ring=2) == g4.ERR_SHAPE
+
+
+def test_decode_noalloc_validation():
+    """The no-workspace decode validates like g4attn_decode, before any HIP call."""
+    lib = g4.load()
+    d = _desc()
+
+    def call(q=FAKE, k=FAKE, v=FAKE, kv_len=FAKE, B=2, max_len=100, cap=128, out=FAKE, splits=0, desc=d):
+        return lib.g4attn_decode_noalloc(ctypes.byref(desc), q, k, v, kv_len, B, max_len, cap, out, None,
+                                         splits, None)
+    assert call(q=None) == g4.ERR_NULL
+    assert call(kv_len=None) == g4.ERR_NULL
+    assert call(B=0) == g4.ERR_SHAPE
+    assert call(max_len=200) == g4.ERR_CACHE_OVERFLOW
+    assert call(out=MISALIGNED) == g4.ERR_LAYOUT
+    assert call(desc=_desc(num_q_heads=30)) == g4.ERR_SHAPE
+    # partial results beyond the 32 MiB scratch array, even as one split
+    assert call(B=4096, max_len=64, cap=64) == g4.ERR_WORKSPACE
+    # an explicit split count whose partial results do not fit
+    assert call(B=64, max_len=100000, cap=100000, splits=64) == g4.ERR_WORKSPACE
