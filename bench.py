@@ -12,6 +12,12 @@ inputs resident in HBM:
                     32 q / 4 KV heads, D=512, one cache tensor for K and V:
                     q prologue at position = cache length + split-KV decode
 
+and, reported beside them, the E2B sliding (B=1, S=1024, 8 q / 1 KV head,
+D=256, window 512) and E2B global (B=1, S=8192, 8 q / 1 KV head, D=512,
+separate K and V) prefills, the 31B sliding decode over rolling caches, the
+31B sliding and K=V chunked prefills over caches, the image-span prefill and
+the K=V decode over the raw-projection cache.
+
 Prints one JSON line.  ``value`` is the prefill attention throughput
 (algorithmic flops = 4*D per visible (row, key) pair per query head, over
 both prefill calls); the decode stream rate, per-stage timings (median over
@@ -67,7 +73,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["sliding", "global", "decode", "sdecode", "chunk", "image", "rdecode"],
+    ap.add_argument("--only", choices=["sliding", "global", "decode", "sdecode", "chunk", "image", "rdecode",
+                                       "e2b_sliding", "e2b_global", "kvchunk"],
                     default=None,
                     help="time one stage only (profiling aid)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -232,8 +239,36 @@ def build_chunk(torch, g4, gen, c):
                 q=torch.empty_like(q_raw), out=torch.empty_like(q_raw), ws=ws)
 
 
+def build_kv_chunk(torch, g4, gen, c):
+    """Chunked prefill of a K=V layer: the last c.S of c.len_hi positions over the layer's own
+    cache (raw projection X, its inverse RMS and rotated key part; every position written by
+    g4attn_kv_tied_append at set-up, not timed)."""
+    dev = "cuda"
+    total = c.len_hi
+    X = gen.normal_bf16((c.B, total, c.Hkv, c.D), gen.seed_key(c.cfg_id, gen.X), dev)
+    wk = gen.norm_weight(c.D, gen.seed_key(c.cfg_id, gen.WK)).to(dev)
+    xc = torch.empty((c.B, c.Hkv, total, c.D), dtype=torch.bfloat16, device=dev)
+    rc = torch.empty((c.B, c.Hkv, total), dtype=torch.float32, device=dev)
+    krc = torch.empty((c.B, c.Hkv, total, 128), dtype=torch.bfloat16, device=dev)
+    g4.g4attn_kv_tied_append(X, wk, xc, rc, krc, c.theta)
+    del X
+    q_raw = gen.normal_bf16((c.B, c.S, c.Hq, c.D), gen.seed_key(c.cfg_id, gen.Q), dev)
+    wq = gen.norm_weight(c.D, gen.seed_key(c.cfg_id, gen.WQ)).to(dev)
+    desc = g4.layer_desc(c.Hq, c.Hkv, c.D, window=c.window, k_eq_v=True, rotary_dims=c.rotary_dims,
+                         rope_theta=c.theta)
+    p0 = total - c.S
+    ws = torch.empty(g4.g4attn_prefill_workspace_bytes(desc, c.B, c.S), dtype=torch.uint8, device=dev)
+    return dict(c=c, desc=desc, xc=xc, rc=rc, krc=krc, wk=wk, q_raw=q_raw, wq=wq, p0=p0, total=total,
+                pos0=torch.full((c.B,), p0, dtype=torch.int32, device=dev),
+                qlen=torch.full((c.B,), c.S, dtype=torch.int32, device=dev),
+                q=torch.empty_like(q_raw), out=torch.empty_like(q_raw), ws=ws)
+
+
 def build_workloads(torch, g4, gen, W):
-    st = {"sliding": build_prefill(torch, g4, gen, W["31b_sliding_prefill"]),
+    st = {"e2b_sliding": build_prefill(torch, g4, gen, W["e2b_sliding_prefill"]),
+          "e2b_global": build_prefill(torch, g4, gen, W["e2b_global_prefill"]),
+          "kvchunk": build_kv_chunk(torch, g4, gen, W["31b_global_kv_chunk_prefill"]),
+          "sliding": build_prefill(torch, g4, gen, W["31b_sliding_prefill"]),
           "global": build_prefill(torch, g4, gen, W["31b_global_kv_prefill"]),
           "decode": build_decode(torch, g4, gen, W["31b_global_kv_decode"]),
           "sdecode": build_decode(torch, g4, gen, W["31b_sliding_decode"]),
@@ -316,53 +351,140 @@ def run_chunk_attn(g4, s):
                             workspace=s["ws"])
 
 
+def run_kv_chunk_attn(g4, s):
+    g4.g4attn_prefill_chunk_tied(s["desc"], s["q"], s["xc"], s["rc"], s["krc"], s["wk"], s["out"], s["pos0"],
+                                 s["qlen"], s["total"] - 1, workspace=s["ws"])
+
+
 def run_decode_attn(g4, s):
     g4.g4attn_decode(s["desc"], s["q"].view(s["q"].shape[0], s["q"].shape[2], s["q"].shape[3]),
                      s["cache"], s["vcache"], s["kv_len"], s["max_len"], s["out"], workspace=s["ws"])
 
 
-def cpu_baseline(torch, gen, st, budget_s=15.0):
-    """The fp64 oracle on a bounded sample of the K=V global prefill.
+def cpu_info():
+    """Host cores this process may run on, the BLAS thread count and the CPU model."""
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        blas = None
+    model = None
+    try:
+        import subprocess
+        txt = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        for line in txt.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except Exception:
+        pass
+    return cores, blas, model
 
-    Sample: KV group 0 (8 query heads), the last R rows of the sequence (each
-    sees every earlier key), with R doubled until the run takes ~budget_s.
-    The rate counts the same algorithmic flops as the GPU (4*D per visible
-    pair per query head).
+
+def cpu_baseline(torch, gen, st, log, budget_s=10.0):
+    """The fp64 oracle, timed on the host cores, per config, from the same raw
+    (pre-prologue) seeded inputs as the GPU: prologue (RMSNorm + RoPE) and
+    attention are both inside the timed region; the rates count the same
+    algorithmic attention flops (4*D per visible pair per query head) or
+    cache bytes as the GPU's.
+
+    E2B sliding, E2B global and 31B sliding prefill run in full.  The 31B K=V
+    global prefill runs on a row sample (KV group 0, its 8 query heads, the
+    last R rows, each seeing every earlier key; R doubled until the run takes
+    about budget_s), the 31B K=V decode on the first 4 of its 32 sequences
+    (every head, every cached row).  The headline value is the oracle's rate
+    over the two 31B prefill calls (31B sliding in full + the K=V sample),
+    the same quantity as the GPU's value.
     """
     from oracle import attention as oat
     from oracle import norm_rope as onr
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
+    f64 = gen.to_f64
+    torch.cuda.synchronize()
+    per = {}
+
+    def prefill_full(key):
+        s = st[key]
+        c = s["c"]
+        qr, kr, vr = f64(s["q_raw"]), f64(s["k_raw"]), f64(s["v_raw"])
+        wq, wk = f64(s["wq"]), f64(s["wk"])
+        pos = np.tile(np.arange(c.S), (c.B, 1))
+        t0 = time.perf_counter()
+        q = onr.norm_rope(qr, wq, pos, c.rotary_dims, c.theta)
+        k = onr.norm_rope(kr, wk, pos, c.rotary_dims, c.theta)
+        v = onr.norm_rope(vr, None, pos, 0, c.theta)
+        oat.attention_band(q, k, v, c.scale, c.window)
+        dt = time.perf_counter() - t0
+        fl = 4.0 * c.D * visible_pairs(c.S, c.window) * c.Hq * c.B
+        per[c.name] = {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "seconds": round(dt, 2),
+                       "sample": "full (prologue + attention)"}
+        return fl, dt
+
+    for key in ("e2b_sliding", "e2b_global", "sliding"):
+        log(f"oracle: {st[key]['c'].name} in full")
+        fl, dt = prefill_full(key)
+        if key == "sliding":
+            fl_s, dt_s = fl, dt
+
+    # 31B K=V global prefill: KV group 0, last R rows
+    log("oracle: 31b_global_kv_prefill row sample")
     s = st["global"]
     c = s["c"]
     G = c.Hq // c.Hkv
     S = c.S
-    torch.cuda.synchronize()
-    X = gen.to_f64(s["X"][0, :, 0])                         # [S, D] raw tied projection, group 0
-    q = gen.to_f64(s["q"][0, :, :G])                        # [S, G, D] post-prologue queries
-    wk = gen.to_f64(s["wk"])
-    t0 = time.perf_counter()
-    K, V = onr.kv_tied_k_v(X[None, :, None, :], wk, np.arange(S)[None, :], c.rotary_dims, c.theta)
-    t_pro = time.perf_counter() - t0
-    R, done_pairs, elapsed = 16, 0, 0.0
+    X = f64(s["X"][0:1, :, 0:1])                      # [1, S, 1, D] raw tied projection, group 0
+    wk, wq = f64(s["wk"]), f64(s["wq"])
+    R = 16
     while True:
         rows = np.arange(S - R, S)
+        qr = f64(s["q_raw"][0:1, S - R:, :G])          # [1, R, G, D]
         t0 = time.perf_counter()
-        oat.attention_band(q[None, :, :, :], K, V, c.scale, 0, rows=rows)
+        K, V = onr.kv_tied_k_v(X, wk, np.arange(S)[None, :], c.rotary_dims, c.theta)
+        q = onr.norm_rope(qr, wq, rows[None, :], c.rotary_dims, c.theta)
+        qfull = np.zeros((1, S, G, c.D))
+        qfull[0, S - R:] = q[0]
+        oat.attention_band(qfull, K, V, c.scale, 0, rows=rows)
         dt = time.perf_counter() - t0
-        pairs = int(((rows + 1).sum())) * G
-        if dt > budget_s / 3 or R >= 4096:
-            done_pairs, elapsed = pairs, dt
+        pairs = int((rows + 1).sum()) * G
+        if dt > budget_s / 3 or R >= min(4096, S):
             break
-        R *= 2
-    tflops = 4.0 * c.D * done_pairs / elapsed / 1e12
-    return {"value": tflops, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"31B K=V global prefill, KV group 0 ({G} q heads), last {R} rows x all "
-                      f"earlier keys ({done_pairs} visible pairs) in {elapsed:.2f}s; K/V prologue of "
-                      f"the group {t_pro:.2f}s not counted"}
+        R = min(2 * R, S)
+    fl_g = 4.0 * c.D * pairs
+    per[c.name] = {"value": round(fl_g / dt / 1e12, 5), "unit": "TFLOP/s", "seconds": round(dt, 2),
+                   "sample": f"KV group 0 ({G} q heads), last {R} rows x all earlier keys ({pairs} visible "
+                             f"pairs of {visible_pairs(S, 0) * c.Hq}); K/V prologue of the group's {S} rows "
+                             f"and the rows' q prologue included"}
+
+    # 31B K=V decode: the first 4 sequences
+    log("oracle: 31b_global_kv_decode, 4 sequences")
+    s = st["decode"]
+    c = s["c"]
+    nseq = 4
+    t_dec, nbytes = 0.0, 0.0
+    for b in range(nseq):
+        nb = int(s["n"][b])
+        kc = f64(s["cache"][b:b + 1, :, :nb])          # [1, Hkv, n_b, D]
+        qr = f64(s["q_raw"][b:b + 1])                  # [1, 1, Hq, D]
+        t0 = time.perf_counter()
+        q = onr.norm_rope(qr, f64(s["wq"]), np.array([[int(s["L"][b])]]), c.rotary_dims, c.theta)
+        oat.decode_attention(q[:, 0], kc, kc, np.array([nb]), c.scale)
+        t_dec += time.perf_counter() - t0
+        nbytes += float(nb) * c.Hkv * c.D * 2 + 2.0 * c.Hq * c.D * 2
+        del kc
+    per[c.name] = {"value": round(nbytes / t_dec / 1e9, 4), "unit": "GB/s", "seconds": round(t_dec, 2),
+                   "sample": f"sequences 0..{nseq - 1} of {c.B} (lengths {[int(x) for x in s['n'][:nseq]]}), "
+                             f"every head and cached row, q prologue included"}
+
+    cores, blas, model = cpu_info()
+    value = (fl_s + fl_g) / (dt_s + dt) / 1e12
+    return {"value": round(value, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": "31B sliding prefill in full + 31B K=V global prefill row sample "
+                      f"({per['31b_global_kv_prefill']['sample']}); fp64 numpy, prologue + attention timed",
+            "blas_threads": blas, "cpu_model": model, "per_config": per}
+
+
+def _r(res, key, nd):
+    return round(res[key], nd) if key in res else None
 
 
 def main():
@@ -385,14 +507,17 @@ def main():
     st = build_workloads(torch, g4, gen, WORKLOADS)
     log("inputs ready")
 
-    plan = [("sliding_prologue", run_sliding, "sliding"), ("sliding_attn", run_sliding_attn, "sliding"),
+    plan = [("e2b_sliding_prologue", run_sliding, "e2b_sliding"), ("e2b_sliding_attn", run_sliding_attn, "e2b_sliding"),
+            ("e2b_global_prologue", run_sliding, "e2b_global"), ("e2b_global_attn", run_sliding_attn, "e2b_global"),
+            ("sliding_prologue", run_sliding, "sliding"), ("sliding_attn", run_sliding_attn, "sliding"),
             ("global_prologue", run_global_pro, "global"), ("global_attn", run_global_attn, "global"),
             ("decode_prologue", run_decode_pro, "decode"), ("decode_attn", run_decode_attn, "decode"),
             ("sliding_decode_prologue", run_decode_pro, "sdecode"),
             ("sliding_decode_attn", run_decode_attn, "sdecode"),
             ("chunk_prologue", run_chunk_pro, "chunk"), ("chunk_attn", run_chunk_attn, "chunk"),
             ("image_prologue", run_sliding, "image"), ("image_attn", run_image_attn, "image"),
-            ("raw_decode_prologue", run_decode_pro, "rdecode"), ("raw_decode_attn", run_decode_raw_attn, "rdecode")]
+            ("raw_decode_prologue", run_decode_pro, "rdecode"), ("raw_decode_attn", run_decode_raw_attn, "rdecode"),
+            ("kv_chunk_prologue", run_chunk_pro, "kvchunk"), ("kv_chunk_attn", run_kv_chunk_attn, "kvchunk")]
     if args.only:
         plan = [p for p in plan if p[2] == args.only]
 
@@ -455,6 +580,16 @@ def main():
     fl_image = 4.0 * ci.D * span_pairs(ci.S, ci.window, *gen.image_spans(ci.S, ci.images)) * ci.Hq * ci.B
     if "image_attn" in avg:
         res["image_prefill_tflops"] = fl_image / avg["image_attn"] / 1e9
+    for key in ("e2b_sliding", "e2b_global"):
+        ce = st[key]["c"]
+        if key + "_attn" in avg:
+            fl = 4.0 * ce.D * visible_pairs(ce.S, ce.window) * ce.Hq * ce.B
+            res[key + "_prefill_tflops"] = fl / avg[key + "_attn"] / 1e9
+    ck = st["kvchunk"]["c"]
+    # row p of the chunk sees every key 0..p
+    fl_kvchunk = 4.0 * ck.D * sum(p + 1 for p in range(ck.len_hi - ck.S, ck.len_hi)) * ck.Hq * ck.B
+    if "kv_chunk_attn" in avg:
+        res["kv_chunk_prefill_tflops"] = fl_kvchunk / avg["kv_chunk_attn"] / 1e9
     rd, crd = st["rdecode"], st["rdecode"]["c"]
     # X row (2 D bytes) + rotated key part (256 bytes) + inverse RMS (4 bytes) per row per KV head
     rdec_bytes = float(rd["n"].sum()) * crd.Hkv * (crd.D * 2 + 256 + 4) + 2.0 * crd.B * crd.Hq * crd.D * 2
@@ -496,6 +631,12 @@ def main():
         "raw_kv_decode_GBps": round(res["raw_kv_decode_GBps"], 1) if "raw_kv_decode_GBps" in res else None,
         "sliding_prefill_tflops": round(res.get("sliding_prefill_tflops", 0.0), 2) if "sliding_prefill_tflops" in res else None,
         "global_prefill_tflops": round(res.get("global_prefill_tflops", 0.0), 2) if "global_prefill_tflops" in res else None,
+        "e2b_sliding_prefill_tflops": _r(res, "e2b_sliding_prefill_tflops", 2),
+        "e2b_global_prefill_tflops": _r(res, "e2b_global_prefill_tflops", 2),
+        "kv_chunk_prefill_tflops": _r(res, "kv_chunk_prefill_tflops", 2),
+        # every prefill rate as a fraction of the bf16 dense MFMA peak, every decode rate of HBM peak
+        "frac_of_peak": {k: round(v / (PEAK_HBM_GBPS if k.endswith("GBps") else PEAK_BF16_TFLOPS), 4)
+                         for k, v in sorted(res.items())},
         "stage_ms": {k: round(v, 4) for k, v in avg.items()},
         "stage_ms_min": {k: round(v, 4) for k, v in mins.items()},
         "roofline": roof,
@@ -508,7 +649,7 @@ def main():
         out["attainable"] = att
     if not args.no_cpu_baseline and "global_attn" in avg:
         log("timing the CPU oracle on a sample")
-        out["cpu_baseline"] = cpu_baseline(torch, gen, st)
+        out["cpu_baseline"] = cpu_baseline(torch, gen, st, log)
     print(json.dumps(out))
 
 

@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libg4attn.so")
 OK, ERR_NULL, ERR_SHAPE, ERR_LAYOUT, ERR_UNSUPPORTED, ERR_CACHE_OVERFLOW, ERR_WORKSPACE, ERR_HIP = range(8)
 
 EXPORTED = ("g4attn_norm_rope", "g4attn_prefill_workspace_bytes", "g4attn_prefill", "g4attn_prefill_chunk",
+            "g4attn_prefill_chunk_tied",
             "g4attn_decode_workspace_bytes", "g4attn_decode", "g4attn_decode_noalloc", "g4attn_kv_tied_append",
             "g4attn_decode_tied",
             "g4attn_status_str",
@@ -91,6 +92,10 @@ def load(path=None):
     lib.g4attn_prefill_chunk.argtypes = [ctypes.POINTER(LayerDesc), _P, _P, _P, ctypes.c_int32, _P, _P,
                                          ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P,
                                          ctypes.c_size_t, _P]
+    lib.g4attn_prefill_chunk_tied.restype = ctypes.c_int
+    lib.g4attn_prefill_chunk_tied.argtypes = [ctypes.POINTER(LayerDesc), _P, _P, _P, _P, _P, ctypes.c_int32, _P,
+                                              _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
+                                              _P, _P, _P, ctypes.c_size_t, _P]
     lib.g4attn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.g4attn_decode_workspace_bytes.argtypes = [ctypes.POINTER(LayerDesc), ctypes.c_int32,
                                                   ctypes.c_int32, ctypes.c_int32]
@@ -275,6 +280,50 @@ def g4attn_prefill_chunk(desc, q, k_cache, v_cache, out, pos0, qlen, max_pos=Non
                                   _ptr(pos0), _ptr(qlen), max_pos, lo, hi, _ptr(out), _ptr(lse), B, S,
                                   _bsh_strides(q), _bsh_strides(out), _ptr(workspace), wbytes, _stream(stream))
     _raise(st, "g4attn_prefill_chunk")
+    return out
+
+
+def g4attn_prefill_chunk_tied(desc, q, x_cache, r_cache, krot_cache, w_k, out, pos0, qlen, max_pos=None, lse=None,
+                              workspace=None, stream=None, span_lo=None, span_hi=None):
+    """Chunked prefill of a K=V layer over its raw-projection cache; see
+    g4attn_prefill_chunk_tied in g4attn.h.  Returns ``out``.
+
+    ``q``/``out`` [B, S, Hq, 512]; ``x_cache`` [B, Hkv, cap, 512], ``r_cache``
+    fp32 [B, Hkv, cap], ``krot_cache`` [B, Hkv, cap, 128] (as
+    g4attn_kv_tied_append writes them), all contiguous; ``pos0``, ``qlen``
+    int32 device tensors [B]; ``max_pos`` as in :func:`g4attn_prefill_chunk`.
+    """
+    lib = load()
+    _check_bf16(q, x_cache, krot_cache, w_k, out)
+    B, S = q.shape[0], q.shape[1]
+    Hq, Hkv, D = desc.num_q_heads, desc.num_kv_heads, desc.head_dim
+    cap = x_cache.shape[2]
+    _expect(q, (B, S, Hq, D), "q")
+    _expect(out, (B, S, Hq, D), "out")
+    _expect(x_cache, (B, Hkv, cap, D), "x_cache")
+    _expect(r_cache, (B, Hkv, cap), "r_cache", torch.float32)
+    _expect(krot_cache, (B, Hkv, cap, 128), "krot_cache")
+    _expect(w_k, (D,), "w_k")
+    _expect(pos0, (B,), "pos0", torch.int32)
+    _expect(qlen, (B,), "qlen", torch.int32)
+    _expect(lse, (B, Hq, S), "lse", torch.float32)
+    _expect(span_lo, (B, S), "span_lo")
+    _expect(span_hi, (B, S), "span_hi")
+    for t in (x_cache, r_cache, krot_cache, w_k):
+        if not t.is_contiguous():
+            raise ValueError("caches and w_k must be contiguous")
+    if max_pos is None:
+        max_pos = int((pos0.to(torch.int64) + qlen.to(torch.int64)).max().item()) - 1
+    need = lib.g4attn_prefill_workspace_bytes(ctypes.byref(desc), B, S)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    lo, hi = _spans(span_lo, span_hi)
+    st = lib.g4attn_prefill_chunk_tied(ctypes.byref(desc), _ptr(q), _ptr(x_cache), _ptr(r_cache),
+                                       _ptr(krot_cache), _ptr(w_k), cap, _ptr(pos0), _ptr(qlen), max_pos, lo, hi,
+                                       _ptr(out), _ptr(lse), B, S, _bsh_strides(q), _bsh_strides(out),
+                                       _ptr(workspace), wbytes, _stream(stream))
+    _raise(st, "g4attn_prefill_chunk_tied")
     return out
 
 

@@ -233,7 +233,6 @@ g4attn_status g4attn_prefill(const g4attn_layer_desc* d, const g4attn_bf16* q,
   if (st != G4ATTN_OK) return st;
   if (!q || !k || !out || !q_strides || !kv_strides || !o_strides) return G4ATTN_ERR_NULL;
   if (!span_lo != !span_hi) return G4ATTN_ERR_NULL;        // spans come as a pair
-  if (span_lo && d->k_eq_v) return G4ATTN_ERR_UNSUPPORTED;
   if (d->k_eq_v) {
     if (!w_k) return G4ATTN_ERR_NULL;
     if (v) return G4ATTN_ERR_SHAPE;  // K=V takes one tensor
@@ -287,9 +286,43 @@ g4attn_status g4attn_prefill(const g4attn_layer_desc* d, const g4attn_bf16* q,
     for (int i = 0; i < 3; ++i) p.xs[i] = kv_strides[i];
     st = hip_status(g4attn::launch_kv_prep(p, s));
     if (st != G4ATTN_OK) return st;
-    a.r = r; a.krot = krot;
+    a.r = r; a.krot = krot; a.kv_rows = S;
   }
   return hip_status(g4attn::launch_prefill(a, s));
+}
+
+// Checks and arguments both chunked prefills share (queries, positions,
+// spans, outputs, workspace); the caller adds its caches and scale.
+static g4attn_status chunk_args(const g4attn_layer_desc* d, const g4attn_bf16* q, int32_t cache_cap,
+                                const int32_t* pos0, const int32_t* qlen, int32_t max_pos, const int32_t* span_lo,
+                                const int32_t* span_hi, g4attn_bf16* out, float* lse, int32_t B, int32_t S,
+                                const int64_t q_strides[3], const int64_t o_strides[3], void* workspace,
+                                size_t workspace_bytes, g4attn::PrefillArgs& a) {
+  if (!q || !pos0 || !qlen || !out || !q_strides || !o_strides) return G4ATTN_ERR_NULL;
+  if (!span_lo != !span_hi) return G4ATTN_ERR_NULL;
+  if (B < 1 || S < 1 || B > 65535 || cache_cap < 1 || max_pos < 0) return G4ATTN_ERR_SHAPE;
+  if ((int64_t)S * (d->num_q_heads / d->num_kv_heads) > (int64_t)INT32_MAX) return G4ATTN_ERR_SHAPE;
+  if (max_pos >= cache_cap) return G4ATTN_ERR_CACHE_OVERFLOW;
+  if (!aligned16(q) || !aligned16(out) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return G4ATTN_ERR_LAYOUT;
+  if (!strides_ok(q_strides) || !strides_ok(o_strides)) return G4ATTN_ERR_LAYOUT;
+  // only the flags: a chunk reads its key side data from the caches
+  const size_t need = prefill_ws(d, B, S).r;
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return G4ATTN_ERR_WORKSPACE;
+  a = g4attn::PrefillArgs{};
+  a.q = q; a.out = out; a.lse = lse;
+  a.pos0 = pos0; a.qlen = qlen; a.max_pos = max_pos;
+  a.span_lo = span_lo; a.span_hi = span_hi;
+  a.B = B; a.S = S; a.Hq = d->num_q_heads; a.Hkv = d->num_kv_heads; a.D = d->head_dim;
+  a.window = d->window; a.kv_tied = d->k_eq_v;
+  a.qmul = 1.f; a.omul = 1.f;
+  // caches [B, Hkv, cap, D]: batch, key (row) and head strides in elements
+  a.ks[0] = (int64_t)d->num_kv_heads * cache_cap * d->head_dim;
+  a.ks[1] = d->head_dim;
+  a.ks[2] = (int64_t)cache_cap * d->head_dim;
+  for (int i = 0; i < 3; ++i) { a.qs[i] = q_strides[i]; a.os[i] = o_strides[i]; }
+  a.flags = (int*)workspace;
+  return G4ATTN_OK;
 }
 
 g4attn_status g4attn_prefill_chunk(const g4attn_layer_desc* d, const g4attn_bf16* q,
@@ -301,35 +334,47 @@ g4attn_status g4attn_prefill_chunk(const g4attn_layer_desc* d, const g4attn_bf16
                                    size_t workspace_bytes, void* stream) {
   g4attn_status st = desc_check(d);
   if (st != G4ATTN_OK) return st;
-  if (!q || !k_cache || !v_cache || !pos0 || !qlen || !out || !q_strides || !o_strides) return G4ATTN_ERR_NULL;
-  if (!span_lo != !span_hi) return G4ATTN_ERR_NULL;
-  if (d->k_eq_v) return G4ATTN_ERR_UNSUPPORTED;  // a K=V cache would hold X and its side data
-  if (B < 1 || S < 1 || B > 65535 || cache_cap < 1 || max_pos < 0) return G4ATTN_ERR_SHAPE;
-  if ((int64_t)S * (d->num_q_heads / d->num_kv_heads) > (int64_t)INT32_MAX) return G4ATTN_ERR_SHAPE;
-  if (max_pos >= cache_cap) return G4ATTN_ERR_CACHE_OVERFLOW;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
-      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
-    return G4ATTN_ERR_LAYOUT;
-  if (!strides_ok(q_strides) || !strides_ok(o_strides)) return G4ATTN_ERR_LAYOUT;
-  const PrefillWs ws = prefill_ws(d, B, S);
-  if (!workspace || workspace_bytes < ws.total || !aligned16(workspace)) return G4ATTN_ERR_WORKSPACE;
-
-  g4attn::PrefillArgs a{};
-  a.q = q; a.k = k_cache; a.v = v_cache; a.out = out; a.lse = lse;
-  a.pos0 = pos0; a.qlen = qlen; a.max_pos = max_pos;
-  a.span_lo = span_lo; a.span_hi = span_hi;
-  a.B = B; a.S = S; a.Hq = d->num_q_heads; a.Hkv = d->num_kv_heads; a.D = d->head_dim;
-  a.window = d->window; a.kv_tied = 0;
+  if (!k_cache || !v_cache) return G4ATTN_ERR_NULL;
+  if (d->k_eq_v) return G4ATTN_ERR_UNSUPPORTED;  // its cache is g4attn_prefill_chunk_tied's
+  g4attn::PrefillArgs a;
+  st = chunk_args(d, q, cache_cap, pos0, qlen, max_pos, span_lo, span_hi, out, lse, B, S, q_strides, o_strides,
+                  workspace, workspace_bytes, a);
+  if (st != G4ATTN_OK) return st;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return G4ATTN_ERR_LAYOUT;
+  a.k = k_cache; a.v = v_cache;
   a.scale_log2 = d->scale * g4attn::kLog2e;
   if (a.scale_log2 == 0.f) a.scale_log2 = 0x1p-126f;
   a.mask_s = a.scale_log2 < 0.f ? INFINITY : -INFINITY;
-  a.qmul = 1.f; a.omul = 1.f;
-  // caches [B, Hkv, cap, D]: batch, key (row) and head strides in elements
-  a.ks[0] = (int64_t)d->num_kv_heads * cache_cap * d->head_dim;
-  a.ks[1] = d->head_dim;
-  a.ks[2] = (int64_t)cache_cap * d->head_dim;
-  for (int i = 0; i < 3; ++i) { a.qs[i] = q_strides[i]; a.os[i] = o_strides[i]; }
-  a.flags = (int*)((char*)workspace + ws.flags);
+  return hip_status(g4attn::launch_prefill(a, (hipStream_t)stream));
+}
+
+g4attn_status g4attn_prefill_chunk_tied(const g4attn_layer_desc* d, const g4attn_bf16* q,
+                                        const g4attn_bf16* x_cache, const float* r_cache,
+                                        const g4attn_bf16* krot_cache, const g4attn_bf16* w_k, int32_t cache_cap,
+                                        const int32_t* pos0, const int32_t* qlen, int32_t max_pos,
+                                        const int32_t* span_lo, const int32_t* span_hi, g4attn_bf16* out,
+                                        float* lse, int32_t B, int32_t S, const int64_t q_strides[3],
+                                        const int64_t o_strides[3], void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  g4attn_status st = desc_check(d);
+  if (st != G4ATTN_OK) return st;
+  if (!x_cache || !r_cache || !krot_cache || !w_k) return G4ATTN_ERR_NULL;
+  if (!d->k_eq_v || d->head_dim != 512 || d->rotary_dims != 128) return G4ATTN_ERR_UNSUPPORTED;
+  if (!(fabsf(d->scale) <= 0x1p30f)) return G4ATTN_ERR_UNSUPPORTED;
+  g4attn::PrefillArgs a;
+  st = chunk_args(d, q, cache_cap, pos0, qlen, max_pos, span_lo, span_hi, out, lse, B, S, q_strides, o_strides,
+                  workspace, workspace_bytes, a);
+  if (st != G4ATTN_OK) return st;
+  if (!aligned16(x_cache) || !aligned16(krot_cache) || !aligned16(w_k) ||
+      (reinterpret_cast<uintptr_t>(r_cache) & 3u))
+    return G4ATTN_ERR_LAYOUT;
+  a.k = x_cache; a.v = nullptr; a.w_k = w_k;
+  a.r = r_cache; a.krot = krot_cache; a.kv_rows = cache_cap;
+  // The cached r carries no logit scale, so scale * log2(e) rides on the
+  // queries; the key factor r > 0 keeps -inf for masked slots.
+  a.scale_log2 = d->scale * g4attn::kLog2e;
+  a.qmul = a.scale_log2;
+  a.mask_s = -INFINITY;
   return hip_status(g4attn::launch_prefill(a, (hipStream_t)stream));
 }
 

@@ -205,8 +205,10 @@ struct PrefillArgs {
   const uint16_t* k;        // K, or X (K=V)
   const uint16_t* v;        // V (NULL for K=V)
   const uint16_t* w_k;      // K=V only
-  const float* r;           // K=V only: [B, Hkv, S] inverse RMS of each key row times scale_log2
-  const uint16_t* krot;     // K=V only: [B, Hkv, S, 128]
+  const float* r;           // K=V only: [B, Hkv, kv_rows] inverse RMS of each key row (times scale_log2
+                            // in a whole-sequence prefill)
+  const uint16_t* krot;     // K=V only: [B, Hkv, kv_rows, 128]
+  int kv_rows;              // K=V only: rows per (b, g) of r and krot (S, or the cache capacity)
   int* flags;               // [B, Hkv, ntiles, 4] per-wave reference-overflow flags
   const int32_t* pos0;      // NULL, or [B] first query position of each sequence (keys from caches)
   const int32_t* qlen;      // NULL, or [B] valid query rows of each sequence (the rest is padding)

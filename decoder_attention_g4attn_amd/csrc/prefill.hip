@@ -106,7 +106,7 @@ __device__ __forceinline__ TileSrc tile_src(const PrefillArgs& a, int kt, int b,
   const int64_t e = b * a.ks[0] + g * a.ks[2] + (int64_t)key0 * a.ks[1];
   t.k = (const char*)(a.k + e);
   t.v = TIED ? nullptr : (const char*)(a.v + e);
-  const int64_t row0 = ((int64_t)b * a.Hkv + g) * a.S + key0;
+  const int64_t row0 = ((int64_t)b * a.Hkv + g) * a.kv_rows + key0;
   t.krot = TIED ? (const char*)(a.krot + row0 * 128) : nullptr;
   t.r = TIED ? a.r + row0 : nullptr;
   // Only rows 0..kBN-1 of the tile are copied, so the clamp row never needs
@@ -962,7 +962,10 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   };
   const bool chunk = a.pos0 != nullptr || a.span_lo != nullptr;  // the extended variant
   for (int redo = 0; redo < 2; ++redo) {
-    if (a.kv_tied)
+    if (a.kv_tied && chunk)
+      hipLaunchKernelGGL((redo ? prefill_kernel<512, true, true, true> : prefill_kernel<512, true, false, true>),
+                         redo ? redo_grid(grid) : grid, dim3(256), 0, st, a);
+    else if (a.kv_tied)
       hipLaunchKernelGGL((redo ? prefill_kernel<512, true, true, false> : prefill_kernel<512, true, false, false>),
                          redo ? redo_grid(grid) : grid, dim3(256), 0, st, a);
     else if (a.D == 512 && chunk)

@@ -82,6 +82,12 @@ WORKLOADS = {
         "31b_global_kv_decode_raw", 9, "decode", B=32, S=1, Hq=32, Hkv=4, D=512,
         window=0, rotary_dims=128, theta=1e6, k_eq_v=True,
         len_lo=32768, len_hi=131072),
+    # chunked prefill of the 31B K=V global layer: the last 4096 of 32768
+    # positions over the layer's own raw-projection cache holding all of them
+    "31b_global_kv_chunk_prefill": Workload(
+        "31b_global_kv_chunk_prefill", 10, "chunk", B=1, S=4096, Hq=32, Hkv=4, D=512,
+        window=0, rotary_dims=128, theta=1e6, k_eq_v=True,
+        len_lo=32768, len_hi=32768),
     # sliding-layer decode of the same 31B batch over rolling caches
     "31b_sliding_decode": Workload(
         "31b_sliding_decode", 6, "decode", B=32, S=1, Hq=32, Hkv=16, D=256,

@@ -6,8 +6,9 @@
  *                       full or zero-padded partial RoPE;
  *   g4attn_prefill    - causal / sliding-window GQA softmax attention over a
  *                       whole prompt, including the K=V global layer;
- *   g4attn_prefill_chunk - the same for a chunk of new positions over
- *                       caches (chunked prefill, padded batches);
+ *   g4attn_prefill_chunk, g4attn_prefill_chunk_tied - the same for a chunk
+ *                       of new positions over caches (chunked prefill, padded
+ *                       batches), the second over a K=V layer's cache;
  *   g4attn_decode     - one new query token per sequence over a KV cache
  *                       (split-KV plus a log-sum-exp combine);
  *   g4attn_decode_noalloc - the same without a workspace argument;
@@ -162,9 +163,10 @@ size_t g4attn_prefill_workspace_bytes(const g4attn_layer_desc* desc, int32_t B, 
  *              sees keys span_lo[b,i] .. span_hi[b,i], whatever the window
  *              or causality says.  A text row takes span_lo = span_hi = i.
  *              Requirements (not checked): span_lo[b,i] <= i <= span_hi[b,i]
- *              and both non-decreasing in i (contiguous spans); span_hi is
- *              clamped to S - 1.  Both or neither (else G4ATTN_ERR_NULL);
- *              not with k_eq_v (G4ATTN_ERR_UNSUPPORTED).
+ *              and both non-decreasing in i (contiguous spans).  The kernel
+ *              clamps span_lo below 0 to 0 and span_hi to S - 1, so no key
+ *              outside the sequence is read.  Both or neither (else
+ *              G4ATTN_ERR_NULL); with k_eq_v too.
  *   workspace  >= g4attn_prefill_workspace_bytes(desc, B, S) bytes, 16-byte
  *              aligned (per-wave flags; for K=V also the inverse RMS and
  *              rotated slice of each key row).
@@ -200,14 +202,20 @@ g4attn_status g4attn_prefill(const g4attn_layer_desc* desc, const g4attn_bf16* q
  *   pos0, qlen device int32 [B]: first position and valid rows of each
  *              sequence (qlen[b] <= S).
  *   max_pos    host-known bound of every pos0[b] + qlen[b] - 1; >= cache_cap
- *              is G4ATTN_ERR_CACHE_OVERFLOW.
+ *              is G4ATTN_ERR_CACHE_OVERFLOW.  The kernel clamps the device
+ *              values to it: qlen[b] is taken as min(qlen[b], S,
+ *              max_pos + 1 - pos0[b]) and a sequence with pos0[b] < 0 has no
+ *              rows, so no cache row past max_pos is read; rows cut off this
+ *              way are left unwritten, like padding.
  *   span_lo,   NULL, or [B, S] bidirectional spans as in g4attn_prefill, in
  *   span_hi    absolute positions (row t of the chunk is position
- *              pos0[b] + t); span_hi is clamped to pos0[b] + qlen[b] - 1.
+ *              pos0[b] + t); span_lo below 0 is taken as 0 and span_hi is
+ *              clamped to pos0[b] + qlen[b] - 1.
  *   out        [B, S, Hq, D] bf16, strides o_strides; lse [B, Hq, S] or NULL.
- *   workspace  >= g4attn_prefill_workspace_bytes(desc, B, S) bytes.
- * K=V layers are G4ATTN_ERR_UNSUPPORTED here (their cache would hold the raw
- * projection and its side data).
+ *   workspace  >= g4attn_prefill_workspace_bytes(desc, B, S) bytes, 16-byte
+ *              aligned (only its per-wave flags are used here).
+ * K=V layers (desc k_eq_v = 1) are G4ATTN_ERR_UNSUPPORTED here: their cache
+ * holds the raw projection and its side data (g4attn_prefill_chunk_tied).
  */
 g4attn_status g4attn_prefill_chunk(const g4attn_layer_desc* desc, const g4attn_bf16* q,
                                    const g4attn_bf16* k_cache, const g4attn_bf16* v_cache, int32_t cache_cap,
@@ -216,6 +224,35 @@ g4attn_status g4attn_prefill_chunk(const g4attn_layer_desc* desc, const g4attn_b
                                    g4attn_bf16* out, float* lse, int32_t B, int32_t S,
                                    const int64_t q_strides[3], const int64_t o_strides[3], void* workspace,
                                    size_t workspace_bytes, void* stream);
+
+/*
+ * Chunked prefill of a K=V global layer over the cache g4attn_kv_tied_append
+ * writes ("Gemma 4" docs, "What changed from Gemma 3", K=V global MQA;
+ * gemma4-pt-claude README, "KV Cache"): out and lse as in
+ * g4attn_prefill_chunk, with the keys and values of cached row p formed
+ * inside the call as in g4attn_decode_tied:
+ *   K_p = r_p * (X_p * w_k on the unrotated dims | krot_p on the rotated)
+ *   V_p = r_p * X_p
+ * so a prompt can be continued (or a padded batch run) over the layer's own
+ * cache, this chunk's rows appended to it first.
+ *
+ *   x_cache, r_cache, krot_cache, cache_cap  as g4attn_kv_tied_append
+ *              writes them; w_k [512] the K-norm weight.
+ *   q, pos0, qlen, max_pos, span_lo, span_hi, out, lse, B, S, strides,
+ *   workspace  as in g4attn_prefill_chunk (clamps included).
+ * desc: k_eq_v = 1, head_dim 512, rotary_dims 128, |scale| <= 2^30 (else
+ * G4ATTN_ERR_UNSUPPORTED).  The logit scale multiplies the queries (the
+ * cached r carries none), so the scores are formed from
+ * bf16(scale * log2(e) * q) rather than from q.
+ */
+g4attn_status g4attn_prefill_chunk_tied(const g4attn_layer_desc* desc, const g4attn_bf16* q,
+                                        const g4attn_bf16* x_cache, const float* r_cache,
+                                        const g4attn_bf16* krot_cache, const g4attn_bf16* w_k, int32_t cache_cap,
+                                        const int32_t* pos0, const int32_t* qlen, int32_t max_pos,
+                                        const int32_t* span_lo, const int32_t* span_hi, g4attn_bf16* out,
+                                        float* lse, int32_t B, int32_t S, const int64_t q_strides[3],
+                                        const int64_t o_strides[3], void* workspace, size_t workspace_bytes,
+                                        void* stream);
 
 /* Workspace (bytes) that g4attn_decode needs; num_splits as passed to it
  * (a sliding layer's size depends on min(max_kv_len, window) only). */

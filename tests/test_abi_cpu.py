@@ -79,9 +79,9 @@ def test_prefill_validation():
     # flags [1, 4, 1 tile, 4 waves] + r [1, 4, 16] + Krot [1, 4, 16, 128], each 256-byte aligned
     assert need == 256 + 256 + 16 * 4 * 128 * 2
     assert _prefill(kv, wk=FAKE, v=None) == g4.ERR_WORKSPACE
-    # bidirectional spans: both bounds or neither; not on K=V layers
+    # bidirectional spans: both bounds or neither; K=V layers take them too
     assert _prefill(_desc(), span_lo=FAKE) == g4.ERR_NULL
-    assert _prefill(kv, wk=FAKE, v=None, span_lo=FAKE, span_hi=FAKE) == g4.ERR_UNSUPPORTED
+    assert _prefill(kv, wk=FAKE, v=None, span_lo=FAKE, span_hi=FAKE) == g4.ERR_WORKSPACE
     assert _prefill(kv, wk=FAKE, v=None, ws=FAKE, wsb=need - 1) == g4.ERR_WORKSPACE
     assert g4.g4attn_prefill_workspace_bytes(_desc(), 1, 16) == 256
     assert _prefill(_desc()) == g4.ERR_WORKSPACE
@@ -217,3 +217,30 @@ def test_decode_noalloc_validation():
     assert call(B=4096, max_len=64, cap=64) == g4.ERR_WORKSPACE
     # an explicit split count whose partial results do not fit
     assert call(B=64, max_len=100000, cap=100000, splits=64) == g4.ERR_WORKSPACE
+
+
+def test_prefill_chunk_tied_validation():
+    lib = g4.load()
+    qs = I64(16 * 32 * 512, 32 * 512, 512)
+    kv = _desc(k_eq_v=True)
+
+    def call(desc=kv, q=FAKE, xc=FAKE, rc=FAKE, kr=FAKE, wk=FAKE, cap=64, pos0=FAKE, qlen=FAKE, max_pos=40, B=1,
+             S=16, ws=None, wsb=0, lo=None, hi=None):
+        return lib.g4attn_prefill_chunk_tied(ctypes.byref(desc), q, xc, rc, kr, wk, cap, pos0, qlen, max_pos, lo,
+                                             hi, FAKE, None, B, S, qs, qs, ws, wsb, None)
+
+    assert call(xc=None) == g4.ERR_NULL
+    assert call(rc=None) == g4.ERR_NULL
+    assert call(kr=None) == g4.ERR_NULL
+    assert call(wk=None) == g4.ERR_NULL
+    assert call(pos0=None) == g4.ERR_NULL
+    assert call(lo=FAKE) == g4.ERR_NULL                                    # spans come as a pair
+    assert call(desc=_desc()) == g4.ERR_UNSUPPORTED                       # not a K=V layer
+    assert call(desc=_desc(k_eq_v=True, rotary_dims=512)) == g4.ERR_UNSUPPORTED
+    assert call(desc=_desc(k_eq_v=True, scale=2.0 ** 31)) == g4.ERR_UNSUPPORTED
+    assert call(max_pos=64) == g4.ERR_CACHE_OVERFLOW
+    assert call(B=0) == g4.ERR_SHAPE
+    assert call(rc=ctypes.c_void_p(0x100002), ws=FAKE, wsb=1 << 30) == g4.ERR_LAYOUT        # r cache not 4-byte aligned
+    assert call(xc=MISALIGNED, ws=FAKE, wsb=1 << 30) == g4.ERR_LAYOUT
+    # only the flags are needed: [1, 4, 1 tile, 4 waves] ints, 256-byte aligned
+    assert call(ws=FAKE, wsb=255) == g4.ERR_WORKSPACE

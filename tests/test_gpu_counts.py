@@ -72,6 +72,23 @@ def test_full_size_chunk_prefill_counts_every_row(gpu_lib):
             np.testing.assert_array_equal(got[b, h], expect, err_msg=f"chunk b={b} h={h}")
 
 
+def test_full_size_kv_chunk_prefill_counts_every_row(gpu_lib):
+    """The 31B K=V chunk (last 4096 of 32768 positions over the raw-projection cache)."""
+    g4 = gpu_lib
+    c = WORKLOADS["31b_global_kv_chunk_prefill"]
+    s = bench.build_kv_chunk(torch, g4, gen, c)
+    lse = torch.empty((c.B, c.Hq, c.S), dtype=torch.float32, device="cuda")
+    bench.run_chunk_pro(g4, s)
+    g4.g4attn_prefill_chunk_tied(_zero_scale(g4, c), s["q"], s["xc"], s["rc"], s["krc"], s["wk"], s["out"],
+                                 s["pos0"], s["qlen"], s["total"] - 1, lse=lse, workspace=s["ws"])
+    torch.cuda.synchronize()
+    expect = oat.visible_count(s["total"], c.window)[s["p0"]:s["p0"] + c.S]
+    got = _counts(lse)
+    for b in range(c.B):
+        for h in range(c.Hq):
+            np.testing.assert_array_equal(got[b, h], expect, err_msg=f"K=V chunk b={b} h={h}")
+
+
 @pytest.mark.parametrize("name", ["31b_global_kv_decode", "31b_sliding_decode"])
 @pytest.mark.parametrize("splits", [0, 1, 7])
 def test_full_size_decode_counts_every_sequence(gpu_lib, name, splits):

@@ -174,6 +174,40 @@ def test_full_size_chunk_prefill_sampled_rows(gpu_lib):
     assert_parity(np.stack(got_all), np.stack(ref_all), "31b sliding chunk prefill sampled rows")
 
 
+def test_full_size_kv_chunk_prefill_sampled_rows(gpu_lib):
+    """The 31B K=V chunked prefill (last 4096 of 32768 positions over the raw-projection cache), as timed."""
+    g4 = gpu_lib
+    c = WORKLOADS["31b_global_kv_chunk_prefill"]
+    s = bench.build_kv_chunk(torch, g4, gen, c)
+    lse = torch.empty((c.B, c.Hq, c.S), dtype=torch.float32, device="cuda")
+    bench.run_chunk_pro(g4, s)
+    g4.g4attn_prefill_chunk_tied(s["desc"], s["q"], s["xc"], s["rc"], s["krc"], s["wk"], s["out"], s["pos0"],
+                                 s["qlen"], s["total"] - 1, lse=lse, workspace=s["ws"])
+    torch.cuda.synchronize()
+    G = c.Hq // c.Hkv
+    # the oracle's keys and values from the raw rows the cache was built from (same seeded draw)
+    X = gen.normal_bf16((c.B, s["total"], c.Hkv, c.D), gen.seed_key(c.cfg_id, gen.X), "cuda")
+    got_all, ref_all = [], []
+    for g in (0, c.Hkv - 1):
+        K, V = onr.kv_tied_k_v(f64(X[0:1, :, g:g + 1]), f64(s["wk"]), np.arange(s["total"])[None, :],
+                               c.rotary_dims, c.theta)
+        kk, vv = K[0, :, 0], V[0, :, 0]
+        toks = _sample_tokens(c.S, 0, n_rand=6, seed=(c.cfg_id, 0, g))
+        heads = [g * G, g * G + G - 1]
+        for t in toks:
+            p = s["p0"] + int(t)
+            qraw = f64(s["q_raw"][0:1, t:t + 1, heads])
+            q = onr.norm_rope(qraw, f64(s["wq"]), np.array([[p]]), c.rotary_dims, c.theta)
+            for hi_, h in enumerate(heads):
+                sc = c.scale * (kk[:p + 1] @ q[0, 0, hi_])
+                m = sc.max()
+                e = np.exp(sc - m)
+                ref_all.append((e @ vv[:p + 1]) / e.sum())
+                got_all.append(f64(s["out"][0, t, h]))
+                np.testing.assert_allclose(float(lse[0, h, t]), m + np.log(e.sum()), rtol=0, atol=LSE_ATOL)
+    assert_parity(np.stack(got_all), np.stack(ref_all), "31B K=V chunk prefill sampled rows")
+
+
 def test_full_size_raw_kv_decode_sampled_heads(gpu_lib):
     """The 31B K=V decode over the raw-projection cache (X + r + Krot), as timed."""
     g4 = gpu_lib
