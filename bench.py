@@ -264,17 +264,19 @@ def build_kv_chunk(torch, g4, gen, c):
                 q=torch.empty_like(q_raw), out=torch.empty_like(q_raw), ws=ws)
 
 
-def build_workloads(torch, g4, gen, W):
-    st = {"e2b_sliding": build_prefill(torch, g4, gen, W["e2b_sliding_prefill"]),
-          "e2b_global": build_prefill(torch, g4, gen, W["e2b_global_prefill"]),
-          "kvchunk": build_kv_chunk(torch, g4, gen, W["31b_global_kv_chunk_prefill"]),
-          "sliding": build_prefill(torch, g4, gen, W["31b_sliding_prefill"]),
-          "global": build_prefill(torch, g4, gen, W["31b_global_kv_prefill"]),
-          "decode": build_decode(torch, g4, gen, W["31b_global_kv_decode"]),
-          "sdecode": build_decode(torch, g4, gen, W["31b_sliding_decode"]),
-          "chunk": build_chunk(torch, g4, gen, W["31b_sliding_chunk_prefill"]),
-          "image": build_prefill(torch, g4, gen, W["31b_sliding_image_prefill"]),
-          "rdecode": build_decode_raw(torch, g4, gen, W["31b_global_kv_decode_raw"])}
+def build_workloads(torch, g4, gen, W, keys=None):
+    """Inputs of every stage's workload (or of ``keys`` only)."""
+    builders = {"e2b_sliding": (build_prefill, "e2b_sliding_prefill"),
+                "e2b_global": (build_prefill, "e2b_global_prefill"),
+                "kvchunk": (build_kv_chunk, "31b_global_kv_chunk_prefill"),
+                "sliding": (build_prefill, "31b_sliding_prefill"),
+                "global": (build_prefill, "31b_global_kv_prefill"),
+                "decode": (build_decode, "31b_global_kv_decode"),
+                "sdecode": (build_decode, "31b_sliding_decode"),
+                "chunk": (build_chunk, "31b_sliding_chunk_prefill"),
+                "image": (build_prefill, "31b_sliding_image_prefill"),
+                "rdecode": (build_decode_raw, "31b_global_kv_decode_raw")}
+    st = {k: fn(torch, g4, gen, W[name]) for k, (fn, name) in builders.items() if keys is None or k in keys}
     torch.cuda.synchronize()
     return st
 
@@ -504,7 +506,7 @@ def main():
     torch.cuda.set_device(0)
     log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)
     log("generating inputs")
-    st = build_workloads(torch, g4, gen, WORKLOADS)
+    st = build_workloads(torch, g4, gen, WORKLOADS, keys=[args.only] if args.only else None)
     log("inputs ready")
 
     plan = [("e2b_sliding_prologue", run_sliding, "e2b_sliding"), ("e2b_sliding_attn", run_sliding_attn, "e2b_sliding"),
@@ -554,46 +556,47 @@ def main():
     avg = {k: float(np.median(v)) for k, v in ms.items()}
     mins = {k: float(np.min(v)) for k, v in ms.items()}
 
-    cs, cg, cd = st["sliding"]["c"], st["global"]["c"], st["decode"]["c"]
+    W = WORKLOADS
+    cs, cg = W["31b_sliding_prefill"], W["31b_global_kv_prefill"]
     fl_sliding = 4.0 * cs.D * visible_pairs(cs.S, cs.window) * cs.Hq * cs.B
     fl_global = 4.0 * cg.D * visible_pairs(cg.S, 0) * cg.Hq * cg.B
-    dec = st["decode"]
-    dec_bytes = float(dec["n"].sum()) * cd.Hkv * cd.D * 2 + 2.0 * cd.B * cd.Hq * cd.D * 2
-    sdec, csd = st["sdecode"], st["sdecode"]["c"]
-    # separate K and V rings: 2 * D bytes per row per KV head for each
-    sdec_bytes = float(sdec["rows"].sum()) * csd.Hkv * csd.D * 2 * 2 + 2.0 * csd.B * csd.Hq * csd.D * 2
     res = {}
-    if "sliding_attn" in avg:
-        res["sliding_prefill_tflops"] = fl_sliding / avg["sliding_attn"] / 1e9
-    if "global_attn" in avg:
-        res["global_prefill_tflops"] = fl_global / avg["global_attn"] / 1e9
+
+    def prefill_rate(stage, key, flops):
+        if stage in avg:
+            res[key] = flops / avg[stage] / 1e9
+
+    prefill_rate("sliding_attn", "sliding_prefill_tflops", fl_sliding)
+    prefill_rate("global_attn", "global_prefill_tflops", fl_global)
+    for key, name in (("e2b_sliding", "e2b_sliding_prefill"), ("e2b_global", "e2b_global_prefill")):
+        ce = W[name]
+        prefill_rate(key + "_attn", key + "_prefill_tflops",
+                     4.0 * ce.D * visible_pairs(ce.S, ce.window) * ce.Hq * ce.B)
+    cc = W["31b_sliding_chunk_prefill"]
+    # chunk row p sees min(p + 1, window) keys
+    prefill_rate("chunk_attn", "chunk_prefill_tflops",
+                 4.0 * cc.D * sum(min(p + 1, cc.window) for p in range(cc.len_hi - cc.S, cc.len_hi)) * cc.Hq * cc.B)
+    ck = W["31b_global_kv_chunk_prefill"]
+    # K=V chunk row p sees every key 0..p
+    prefill_rate("kv_chunk_attn", "kv_chunk_prefill_tflops",
+                 4.0 * ck.D * sum(p + 1 for p in range(ck.len_hi - ck.S, ck.len_hi)) * ck.Hq * ck.B)
+    ci = W["31b_sliding_image_prefill"]
+    prefill_rate("image_attn", "image_prefill_tflops",
+                 4.0 * ci.D * span_pairs(ci.S, ci.window, *gen.image_spans(ci.S, ci.images)) * ci.Hq * ci.B)
     if "decode_attn" in avg:
+        cd, dec = W["31b_global_kv_decode"], st["decode"]
+        # one cache tensor serves as K and V: D bf16 per row per KV head, plus q in and out
+        dec_bytes = float(dec["n"].sum()) * cd.Hkv * cd.D * 2 + 2.0 * cd.B * cd.Hq * cd.D * 2
         res["decode_GBps"] = dec_bytes / avg["decode_attn"] / 1e6
     if "sliding_decode_attn" in avg:
+        csd, sdec = W["31b_sliding_decode"], st["sdecode"]
+        # separate K and V rings: 2 * D bytes per row per KV head for each
+        sdec_bytes = float(sdec["rows"].sum()) * csd.Hkv * csd.D * 2 * 2 + 2.0 * csd.B * csd.Hq * csd.D * 2
         res["sliding_decode_GBps"] = sdec_bytes / avg["sliding_decode_attn"] / 1e6
-    cc = st["chunk"]["c"]
-    # every chunk row (positions >= window) sees `window` keys
-    fl_chunk = 4.0 * cc.D * sum(min(p + 1, cc.window) for p in range(cc.len_hi - cc.S, cc.len_hi)) * cc.Hq * cc.B
-    if "chunk_attn" in avg:
-        res["chunk_prefill_tflops"] = fl_chunk / avg["chunk_attn"] / 1e9
-    ci = st["image"]["c"]
-    fl_image = 4.0 * ci.D * span_pairs(ci.S, ci.window, *gen.image_spans(ci.S, ci.images)) * ci.Hq * ci.B
-    if "image_attn" in avg:
-        res["image_prefill_tflops"] = fl_image / avg["image_attn"] / 1e9
-    for key in ("e2b_sliding", "e2b_global"):
-        ce = st[key]["c"]
-        if key + "_attn" in avg:
-            fl = 4.0 * ce.D * visible_pairs(ce.S, ce.window) * ce.Hq * ce.B
-            res[key + "_prefill_tflops"] = fl / avg[key + "_attn"] / 1e9
-    ck = st["kvchunk"]["c"]
-    # row p of the chunk sees every key 0..p
-    fl_kvchunk = 4.0 * ck.D * sum(p + 1 for p in range(ck.len_hi - ck.S, ck.len_hi)) * ck.Hq * ck.B
-    if "kv_chunk_attn" in avg:
-        res["kv_chunk_prefill_tflops"] = fl_kvchunk / avg["kv_chunk_attn"] / 1e9
-    rd, crd = st["rdecode"], st["rdecode"]["c"]
-    # X row (2 D bytes) + rotated key part (256 bytes) + inverse RMS (4 bytes) per row per KV head
-    rdec_bytes = float(rd["n"].sum()) * crd.Hkv * (crd.D * 2 + 256 + 4) + 2.0 * crd.B * crd.Hq * crd.D * 2
     if "raw_decode_attn" in avg:
+        crd, rd = W["31b_global_kv_decode_raw"], st["rdecode"]
+        # X row (2 D bytes) + rotated key part (256 bytes) + inverse RMS (4 bytes) per row per KV head
+        rdec_bytes = float(rd["n"].sum()) * crd.Hkv * (crd.D * 2 + 256 + 4) + 2.0 * crd.B * crd.Hq * crd.D * 2
         res["raw_kv_decode_GBps"] = rdec_bytes / avg["raw_decode_attn"] / 1e6
     prefill_ms = avg.get("sliding_attn", 0.0) + avg.get("global_attn", 0.0)
     prefill_fl = (fl_sliding if "sliding_attn" in avg else 0) + (fl_global if "global_attn" in avg else 0)
@@ -623,14 +626,14 @@ def main():
             "value_is": "prefill attention TFLOP/s over the two 31B prefill calls",
             "parallelism": "single GPU",
         },
-        "decode_GBps": round(res.get("decode_GBps", 0.0), 1) if "decode_GBps" in res else None,
+        "decode_GBps": _r(res, "decode_GBps", 1),
         "decode_hbm_frac": round(res["decode_GBps"] / PEAK_HBM_GBPS, 4) if "decode_GBps" in res else None,
-        "sliding_decode_GBps": round(res["sliding_decode_GBps"], 1) if "sliding_decode_GBps" in res else None,
-        "chunk_prefill_tflops": round(res["chunk_prefill_tflops"], 2) if "chunk_prefill_tflops" in res else None,
-        "image_prefill_tflops": round(res["image_prefill_tflops"], 2) if "image_prefill_tflops" in res else None,
-        "raw_kv_decode_GBps": round(res["raw_kv_decode_GBps"], 1) if "raw_kv_decode_GBps" in res else None,
-        "sliding_prefill_tflops": round(res.get("sliding_prefill_tflops", 0.0), 2) if "sliding_prefill_tflops" in res else None,
-        "global_prefill_tflops": round(res.get("global_prefill_tflops", 0.0), 2) if "global_prefill_tflops" in res else None,
+        "sliding_decode_GBps": _r(res, "sliding_decode_GBps", 1),
+        "chunk_prefill_tflops": _r(res, "chunk_prefill_tflops", 2),
+        "image_prefill_tflops": _r(res, "image_prefill_tflops", 2),
+        "raw_kv_decode_GBps": _r(res, "raw_kv_decode_GBps", 1),
+        "sliding_prefill_tflops": _r(res, "sliding_prefill_tflops", 2),
+        "global_prefill_tflops": _r(res, "global_prefill_tflops", 2),
         "e2b_sliding_prefill_tflops": _r(res, "e2b_sliding_prefill_tflops", 2),
         "e2b_global_prefill_tflops": _r(res, "e2b_global_prefill_tflops", 2),
         "kv_chunk_prefill_tflops": _r(res, "kv_chunk_prefill_tflops", 2),
@@ -647,7 +650,7 @@ def main():
         att["global_prefill_frac_of_gemm"] = round(res["global_prefill_tflops"] / att["bf16_gemm_8192_tflops"], 4)
         att["decode_frac_of_copy"] = round(res["decode_GBps"] / att["hbm_copy_GBps"], 4)
         out["attainable"] = att
-    if not args.no_cpu_baseline and "global_attn" in avg:
+    if not args.no_cpu_baseline and args.only is None:
         log("timing the CPU oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(torch, gen, st, log)
     print(json.dumps(out))

@@ -222,8 +222,9 @@ __device__ __forceinline__ void pin(uint32_t& v) { asm volatile("" : "+v"(v)); }
 // S(kt+1) = K(kt+1) Q^T with its MFMAs interleaved with the softmax VALU
 // work of S(kt), then O += V(kt)^T P(kt)^T.  Tiles kt and kt+1 are resident
 // in LDS while tile kt+2 is in flight (NST = 3 stages); configurations
-// whose three stages do not fit (D = 512 without K=V) use two stages and
-// load tile kt+2 after PV(kt).
+// whose three stages do not fit (D = 512 without K=V) use two stages whose
+// K and V halves are refilled a step apart: K(kt+2) and V(kt+1) are in
+// flight during iteration kt.
 // EXT: the extended masks and row layouts: rows that continue sequences
 // over caches (pos0 / qlen) and bidirectional spans (span_lo / span_hi);
 // each is off when its pointer is NULL.
@@ -486,13 +487,18 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     // S^T of the tile in stage so, with the softmax of s_prev spread over its
     // MFMAs: each MFMA is followed by its share of the micro-ops, fenced so the
     // scheduler keeps this order (the ops run while the MFMA does).
-    // With LOADS, the copy of tile ld_kt into stage ld_so rides along, one
-    // piece after every other MFMA.
+    // With LOADS, copies ride along, one piece after every other MFMA: three
+    // stages, all of tile ld_kt into stage ld_so; two stages, the K half of
+    // tile ld_kt into stage ld_so and (v_on) the V half of tile v_kt into
+    // stage v_so.
     // ka[0 .. kLook-1] hold the first K fragments, read by the caller.
     auto qk_softmax = [&](int so, bf16x8 (&ka)[kLook + 1], const f32x16& s_prev, const float (&c)[16],
-                          bf16x8 (&pb)[2], auto loads, int ld_so, int ld_kt) -> f32x16 {
+                          bf16x8 (&pb)[2], auto loads, int ld_so, int ld_kt, int v_so, int v_kt,
+                          bool v_on) -> f32x16 {
       constexpr bool LOADS = decltype(loads)::value;
+      constexpr int PER = D == 512 ? 8 : 4;  // pieces of a K or V half
       const TileSrc ts = tile_src<D, TIED>(a, ld_kt, b, g, key_end);
+      const TileSrc tsv = tile_src<D, TIED>(a, NST == 2 ? v_kt : ld_kt, b, g, key_end);
       const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
       Sm st;
       f32x16 s = f32x16{};
@@ -503,8 +509,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = kSmOps * t / C::NT; j < kSmOps * (t + 1) / C::NT; ++j) sm_op(st, s_prev, c, m_use, j);
-        if (LOADS && (t & 1) == 0 && (t >> 1) < TilePieces<D, TIED>::N)
-          load_piece<D, TIED>(a, ts, lds0 + ld_so, wave, lane, t >> 1);
+        if (LOADS && (t & 1) == 0 && (t >> 1) < TilePieces<D, TIED>::N) {
+          const int p = t >> 1;
+          if (NST == 3 || p < PER)
+            load_piece<D, TIED>(a, ts, lds0 + ld_so, wave, lane, p);
+          else if (v_on)
+            load_piece<D, TIED>(a, tsv, lds0 + v_so, wave, lane, p);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       sm_out(st, pb);
@@ -578,21 +589,25 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       first_visible(s_cur, c, kt);
       if (edge_tile(kt)) mask_edge(s_cur, kt);
       bf16x8 pb[2];
-      // three stages: tile kt+2 goes to the stage tile kt-1 left (past the
-      // end, the last tile is copied again into that unused stage)
-      s_nxt = qk_softmax(so_nxt, ka, s_cur, c, pb, std::integral_constant<bool, NST == 3>{}, so_ld,
-                         min(kt + 2, kt_hi));
+      // Three stages: tile kt+2 goes to the stage tile kt-1 left.  Two
+      // stages: K(kt+2) goes where K(kt) was (its scores were taken in the
+      // last step) and V(kt+1) where V(kt-1) was (the first step's V(kt+1)
+      // came with the first two tiles), so each half has a whole step to
+      // land.  Past the end, the last tile's K is copied again into the
+      // unused K half or stage.
+      s_nxt = qk_softmax(so_nxt, ka, s_cur, c, pb, std::true_type{}, NST == 3 ? so_ld : so_cur,
+                         min(kt + 2, kt_hi), so_nxt, kt + 1, kt > kt_lo);
       __builtin_amdgcn_sched_barrier(0);
       pv(so_cur, pb);
-      if (NST == 2 && kt + 2 <= kt_hi) {
-        __syncthreads();  // every wave is done with tile kt
-        load_tile<D, TIED>(a, lds0 + so_cur, kt + 2, b, g, key_end, wave, lane);
-      }
       const int t = so_cur;
       so_cur = so_nxt;
       if (NST == 3) { so_nxt = so_ld; so_ld = t; } else { so_nxt = t; }
     };
     auto last = [&](f32x16& s_cur) {
+      if (NST == 2) {  // two stages: V(kt_hi) was copied during the last step
+        wait_vmem_all();
+        __syncthreads();
+      }
       float c[16];
       key_mul(so_cur, c);
       first_visible(s_cur, c, kt_hi);
