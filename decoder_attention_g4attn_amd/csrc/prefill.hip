@@ -223,8 +223,8 @@ __device__ __forceinline__ void pin(uint32_t& v) { asm volatile("" : "+v"(v)); }
 // work of S(kt), then O += V(kt)^T P(kt)^T.  Tiles kt and kt+1 are resident
 // in LDS while tile kt+2 is in flight (NST = 3 stages); configurations
 // whose three stages do not fit (D = 512 without K=V) use two stages whose
-// K and V halves are refilled a step apart: K(kt+2) and V(kt+1) are in
-// flight during iteration kt.
+// K and V halves are refilled half a step apart: K(kt+2) and V(kt+1) are
+// copied during iteration kt.
 // EXT: the extended masks and row layouts: rows that continue sequences
 // over caches (pos0 / qlen) and bidirectional spans (span_lo / span_hi);
 // each is off when its pointer is NULL.
@@ -487,18 +487,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     // S^T of the tile in stage so, with the softmax of s_prev spread over its
     // MFMAs: each MFMA is followed by its share of the micro-ops, fenced so the
     // scheduler keeps this order (the ops run while the MFMA does).
-    // With LOADS, copies ride along, one piece after every other MFMA: three
-    // stages, all of tile ld_kt into stage ld_so; two stages, the K half of
-    // tile ld_kt into stage ld_so and (v_on) the V half of tile v_kt into
-    // stage v_so.
+    // Copy pieces 0 .. NQ-1 of the step's loads ride along, one after every
+    // fourth MFMA (issue(p) issues piece p).
     // ka[0 .. kLook-1] hold the first K fragments, read by the caller.
     auto qk_softmax = [&](int so, bf16x8 (&ka)[kLook + 1], const f32x16& s_prev, const float (&c)[16],
-                          bf16x8 (&pb)[2], auto loads, int ld_so, int ld_kt, int v_so, int v_kt,
-                          bool v_on) -> f32x16 {
-      constexpr bool LOADS = decltype(loads)::value;
-      constexpr int PER = D == 512 ? 8 : 4;  // pieces of a K or V half
-      const TileSrc ts = tile_src<D, TIED>(a, ld_kt, b, g, key_end);
-      const TileSrc tsv = tile_src<D, TIED>(a, NST == 2 ? v_kt : ld_kt, b, g, key_end);
+                          bf16x8 (&pb)[2], auto issue, auto nq) -> f32x16 {
+      constexpr int NQ = decltype(nq)::value;
+      static_assert(NQ <= C::NT / 4, "copy slots of the score MFMAs");
       const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
       Sm st;
       f32x16 s = f32x16{};
@@ -509,13 +504,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = kSmOps * t / C::NT; j < kSmOps * (t + 1) / C::NT; ++j) sm_op(st, s_prev, c, m_use, j);
-        if (LOADS && (t & 1) == 0 && (t >> 1) < TilePieces<D, TIED>::N) {
-          const int p = t >> 1;
-          if (NST == 3 || p < PER)
-            load_piece<D, TIED>(a, ts, lds0 + ld_so, wave, lane, p);
-          else if (v_on)
-            load_piece<D, TIED>(a, tsv, lds0 + v_so, wave, lane, p);
-        }
+        if ((t & 3) == 0 && (t >> 2) < NQ) issue(t >> 2);
         __builtin_amdgcn_sched_barrier(0);
       }
       sm_out(st, pb);
@@ -525,9 +514,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     f32x16 oacc[C::NC];
 #pragma unroll
     for (int c = 0; c < C::NC; ++c) oacc[c] = f32x16{};
-    // O^T += V^T P^T over the tile in stage so, transposing reads kLook ahead.
-    auto pv = [&](int so, const bf16x8 (&pb)[2]) {
+    // O^T += V^T P^T over the tile in stage so, transposing reads kLook ahead;
+    // copy pieces P0 .. P0+NP-1 ride along, one after every fourth MFMA.
+    auto pv = [&](int so, const bf16x8 (&pb)[2], auto issue, auto p0, auto np) {
+      constexpr int P0 = decltype(p0)::value, NP = decltype(np)::value;
       constexpr int NPV = 2 * C::NC;  // (mm, c) pairs
+      static_assert(NP <= NPV / 4, "copy slots of the PV MFMAs");
       auto vread = [&](int i) -> bf16x8 {
         const int mm = i / C::NC, c = i % C::NC;
         const i16x4 lo = lds_read_tr16(lds_ptr(so) + toff[mm][0] + 64 * c);
@@ -545,8 +537,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
           mfma_acc<true>(oacc[c], va[i % (kLook + 1)], pb[mm]);
         else
           mfma_acc<false>(oacc[c], va[i % (kLook + 1)], pb[mm]);
+        if ((i & 3) == 1 && (i >> 2) < NP) issue(P0 + (i >> 2));
       }
     };
+    auto no_issue = [](int) {};
 
     if (REDO) {
       // first sweep: the true maximum of every row (stages 0 and 1 hold kt_lo
@@ -576,9 +570,15 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     // of tile kt + 1 into s_nxt.  Written out twice per loop trip with the two
     // score registers swapped, so neither is ever copied.
     int so_cur = 0, so_nxt = C::STAGE, so_ld = NST == 3 ? 2 * C::STAGE : 0;
+    constexpr int PER = D == 512 ? 8 : 4;  // copy pieces of a K or V half
     auto step = [&](int kt, f32x16& s_cur, f32x16& s_nxt) {
-      wait_vmem_all();  // this wave's copies of tile kt+1 have landed
-      __syncthreads();  // all of tile kt+1 is in LDS; every wave is done with tile kt-1
+      // this wave's copies of tile kt+1 (three stages) or of K(kt+1) (two
+      // stages: V(kt), issued after it, may still be in flight) have landed
+      if (NST == 2)
+        wait_vmem<PER>();
+      else
+        wait_vmem_all();
+      __syncthreads();  // ... in every wave; every wave is done with tile kt-1
       // first K fragments of tile kt+1 right away: their latency hides under
       // the bookkeeping below
       bf16x8 ka[kLook + 1];
@@ -589,16 +589,32 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       first_visible(s_cur, c, kt);
       if (edge_tile(kt)) mask_edge(s_cur, kt);
       bf16x8 pb[2];
-      // Three stages: tile kt+2 goes to the stage tile kt-1 left.  Two
-      // stages: K(kt+2) goes where K(kt) was (its scores were taken in the
-      // last step) and V(kt+1) where V(kt-1) was (the first step's V(kt+1)
-      // came with the first two tiles), so each half has a whole step to
-      // land.  Past the end, the last tile's K is copied again into the
-      // unused K half or stage.
-      s_nxt = qk_softmax(so_nxt, ka, s_cur, c, pb, std::true_type{}, NST == 3 ? so_ld : so_cur,
-                         min(kt + 2, kt_hi), so_nxt, kt + 1, kt > kt_lo);
+      // The step's copies, spread over both MFMA runs (neither target is read
+      // in this step).  Three stages: tile kt+2 goes to the stage tile kt-1
+      // left.  Two stages: K(kt+2), during the score MFMAs, goes where K(kt)
+      // was (its scores were taken in the last step), and V(kt+1), during
+      // PV, where V(kt-1) was; V(kt+1) is waited for only before the next
+      // step's PV, so each half has about a step to land.  (The first step
+      // copies V(kt+1) again and, past the end, K(kt_hi) again, into halves
+      // nothing reads, which keeps the count of copies in flight fixed.)
+      constexpr int NP = TilePieces<D, TIED>::N;
+      constexpr int NQ = NST == 2 ? PER : (NP + 1) / 2;  // pieces issued during the score MFMAs
+      const TileSrc tsk = tile_src<D, TIED>(a, min(kt + 2, kt_hi), b, g, key_end);
+      const TileSrc tsv = tile_src<D, TIED>(a, NST == 2 ? kt + 1 : kt_hi, b, g, key_end);
+      const uint32_t st_k = lds0 + (NST == 3 ? so_ld : so_cur), st_v = lds0 + so_nxt;
+      auto issue = [&](int p) {
+        if (NST == 3 || p < PER)
+          load_piece<D, TIED>(a, tsk, st_k, wave, lane, p);
+        else
+          load_piece<D, TIED>(a, tsv, st_v, wave, lane, p);
+      };
+      s_nxt = qk_softmax(so_nxt, ka, s_cur, c, pb, issue, std::integral_constant<int, NQ>{});
       __builtin_amdgcn_sched_barrier(0);
-      pv(so_cur, pb);
+      if (NST == 2) {  // V(kt), copied during the last step's PV, has landed in every wave
+        wait_vmem<PER>();
+        __syncthreads();
+      }
+      pv(so_cur, pb, issue, std::integral_constant<int, NQ>{}, std::integral_constant<int, NP - NQ>{});
       const int t = so_cur;
       so_cur = so_nxt;
       if (NST == 3) { so_nxt = so_ld; so_ld = t; } else { so_nxt = t; }
@@ -614,7 +630,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       if (edge_tile(kt_hi)) mask_edge(s_cur, kt_hi);
       bf16x8 pb[2];
       softmax(s_cur, c, pb);
-      pv(so_cur, pb);
+      pv(so_cur, pb, no_issue, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
     };
     f32x16 sa = qk(0), sb;
     int kt = kt_lo;
