@@ -60,10 +60,11 @@ def test_noalloc_sliding_ring_equals_decode(gpu_lib):
     assert torch.equal(o, o_ref) and torch.equal(l_, l_ref)
 
 
-def test_noalloc_reduces_splits_to_fit_then_smaller_call(gpu_lib):
-    """A batch whose automatic split count needs more than the scratch array:
-    the call runs with the largest smaller count that fits (bit-exact with
-    g4attn_decode at that count); then a small call reuses the array."""
+def test_noalloc_explicit_splits_then_smaller_call(gpu_lib):
+    """An explicit split count whose partial results fit the scratch array is
+    bit-exact with g4attn_decode at that count, the largest such count
+    included; a count that does not fit is refused; then a small call reuses
+    the array."""
     g4 = gpu_lib
     B, Hq, Hkv, D = 32, 32, 4, 512
     desc = g4.layer_desc(Hq, Hkv, D, rotary_dims=128)
@@ -71,12 +72,12 @@ def test_noalloc_reduces_splits_to_fit_then_smaller_call(gpu_lib):
     lens = rng.integers(1000, 8192, size=B, endpoint=True).tolist()
     q, kc, _, kv_len = _case(B, Hq, Hkv, D, lens, 8192, True, 100)
     max_len = max(lens)
-    assert g4.g4attn_decode_workspace_bytes(desc, B, max_len, 0) > SCRATCH
-    # the workspace grows with the split count, so the count the call must pick
-    # is the largest whose workspace fits
+    # the workspace grows with the split count: the largest count that fits
     ns = max(n for n in range(1, 65) if g4.g4attn_decode_workspace_bytes(desc, B, max_len, n) <= SCRATCH)
-    o_ref, l_ref, o, l_ = _both(g4, desc, q, kc, kc, kv_len, max_len, ns)
-    assert torch.equal(o, o_ref) and torch.equal(l_, l_ref)
+    assert 1 < ns < 32
+    for n in (ns, 3):
+        o_ref, l_ref, o, l_ = _both(g4, desc, q, kc, kc, kv_len, max_len, n, n)
+        assert torch.equal(o, o_ref) and torch.equal(l_, l_ref), f"splits={n}"
     # an explicit count that does not fit is refused, nothing launched
     with pytest.raises(g4.G4AttnError) as ei:
         g4.g4attn_decode_noalloc(desc, q, kc, kc, kv_len, max_len, torch.empty_like(q), num_splits=32)
