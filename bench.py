@@ -47,9 +47,9 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 # change, the roofline reports traffic as null until the counters are re-taken.
 PREFILL_TRAFFIC = {
     "sources": ["prefill.hip", "g4attn_internal.h", "norm_rope.hip", "abi.hip"],
-    "sources_sha256": "9f2812a110fbee1ff18fc6febc7452cad9e40226f72bccf90ff6f153001defb5",
-    "fetch_kib": 3.23952e6, "fetch_scale": 2.0,
-    "write_kib": 1.26393e6, "write_scale": 1.0,
+    "sources_sha256": "2128b585b569d067e9ada1d4c289257b99bea7fd63a4b14c5b55b71c80cd1ba2",
+    "fetch_kib": 3.2398e6, "fetch_scale": 2.0,
+    "write_kib": 1.29559e6, "write_scale": 1.0,
 }
 
 
