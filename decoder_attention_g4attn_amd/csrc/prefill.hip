@@ -729,6 +729,7 @@ void prefill_d256_kernel(PrefillArgs a) {
       // the next row tile whose main pass flagged a reference overflow (the
       // flags of tile L = tile + ntiles (g + Hkv b) sit at flags[L * waves])
       const int64_t L = redo.next([&](int64_t c) {
+        static_assert(NW == 4, "four wave flags per row tile");
         const u32x4 f = *(const u32x4*)(a.flags + c * NW);
         return (f[0] | f[1] | f[2] | f[3]) != 0u;
       });
