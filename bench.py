@@ -47,7 +47,7 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 # change, the roofline reports traffic as null until the counters are re-taken.
 PREFILL_TRAFFIC = {
     "sources": ["prefill.hip", "g4attn_internal.h", "norm_rope.hip", "abi.hip"],
-    "sources_sha256": "2128b585b569d067e9ada1d4c289257b99bea7fd63a4b14c5b55b71c80cd1ba2",
+    "sources_sha256": "33d89fbbc31e7c30342dde6c0d9ca96cc92cadc9442c7413291fb3d1e9dcae3f",
     "fetch_kib": 3.2398e6, "fetch_scale": 2.0,
     "write_kib": 1.29559e6, "write_scale": 1.0,
 }
