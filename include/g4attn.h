@@ -286,8 +286,11 @@ size_t g4attn_decode_workspace_bytes(const g4attn_layer_desc* desc, int32_t B,
  *              G4ATTN_ERR_CACHE_OVERFLOW; sliding layer: cache_cap != window
  *              is G4ATTN_ERR_SHAPE.
  *   out        [B, Hq, D] bf16 contiguous;  lse  [B, Hq] fp32 or NULL.
- *   num_splits 0 = automatic; otherwise the row range [0, rows) is cut into
- *              num_splits equal chunks (a multiple of 64 rows each), with
+ *   num_splits 0 = automatic (about one workgroup per compute unit over
+ *              B * Hkv (sequence, KV head) pairs: ceil(256 / (B * Hkv))
+ *              chunks of at least 256 rows); otherwise the row range
+ *              [0, rows) is cut into num_splits equal chunks (a multiple of
+ *              64 rows each), with
  *              rows = max_kv_len (global) or min(max_kv_len, window)
  *              (sliding); the partial results are merged by a log-sum-exp
  *              combine.
