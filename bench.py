@@ -597,6 +597,15 @@ def main():
         # X row (2 D bytes) + rotated key part (256 bytes) + inverse RMS (4 bytes) per row per KV head
         rdec_bytes = float(rd["n"].sum()) * crd.Hkv * (crd.D * 2 + 256 + 4) + 2.0 * crd.B * crd.Hq * crd.D * 2
         res["raw_kv_decode_GBps"] = rdec_bytes / avg["raw_decode_attn"] / 1e6
+    # prologues (norm + RoPE): 2 bytes read and 2 written per element of q (and k, v)
+    pro = {}
+    for stage, name, tensors in (("sliding_prologue", "31b_sliding_prefill", "qkv"),
+                                 ("global_prologue", "31b_global_kv_prefill", "q"),
+                                 ("e2b_global_prologue", "e2b_global_prefill", "qkv")):
+        if stage in avg:
+            cw = W[name]
+            elems = cw.B * cw.S * cw.D * (cw.Hq + (2 * cw.Hkv if tensors == "qkv" else 0))
+            pro[stage] = round(4.0 * elems / avg[stage] / 1e6, 1)
     prefill_ms = avg.get("sliding_attn", 0.0) + avg.get("global_attn", 0.0)
     prefill_fl = (fl_sliding if "sliding_attn" in avg else 0) + (fl_global if "global_attn" in avg else 0)
     value = prefill_fl / prefill_ms / 1e9 if prefill_ms > 0 else None
@@ -637,6 +646,7 @@ def main():
         "e2b_global_prefill_tflops": _r(res, "e2b_global_prefill_tflops", 2),
         "kv_chunk_prefill_tflops": _r(res, "kv_chunk_prefill_tflops", 2),
         # every prefill rate as a fraction of the bf16 dense MFMA peak, every decode rate of HBM peak
+        "prologue_GBps": pro,
         "frac_of_peak": {k: round(v / (PEAK_HBM_GBPS if k.endswith("GBps") else PEAK_BF16_TFLOPS), 4)
                          for k, v in sorted(res.items())},
         "stage_ms": {k: round(v, 4) for k, v in avg.items()},
