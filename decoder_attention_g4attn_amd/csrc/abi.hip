@@ -213,8 +213,8 @@ static PrefillWs prefill_ws(const g4attn_layer_desc* d, int32_t B, int32_t S) {
   const int64_t ntiles = ((int64_t)S * G + 127) / 128;
   const size_t rows = (size_t)B * d->num_kv_heads * S;
   w.flags = 0;
-  // per-wave flags: ntiles 128-row tiles x 4 waves, plus room for the
-  // D = 256 kernel's 256-row tiles of 8 waves (at most ntiles/2 + 1 of them)
+  // per-wave flags: ntiles 128-row tiles x 4 waves (both prefill kernels run
+  // 128-row workgroups of 4 waves), plus two tiles of slack
   w.r = align256((size_t)B * d->num_kv_heads * (ntiles + 2) * 4 * sizeof(int));
   w.krot = w.r + (d->k_eq_v ? align256(rows * sizeof(float)) : 0);
   w.total = w.krot + (d->k_eq_v ? align256(rows * 128 * sizeof(uint16_t)) : 0);
