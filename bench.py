@@ -48,8 +48,8 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 PREFILL_TRAFFIC = {
     "sources": ["prefill.hip", "g4attn_internal.h", "norm_rope.hip", "abi.hip"],
     "sources_sha256": "5a00d9a03b5e9e34e42ba160f2fbb1338b93be66004442aba86c61fabc6faa7c",
-    "fetch_kib": 3.2398e6, "fetch_scale": 2.0,
-    "write_kib": 1.29559e6, "write_scale": 1.0,
+    "fetch_kib": 3.23965e6, "fetch_scale": 2.0,
+    "write_kib": 1.28787e6, "write_scale": 1.0,
 }
 
 
