@@ -395,3 +395,35 @@ def test_decode_batched_equals_single_bit_exact(gpu_lib):
                              o1, lse=l1, num_splits=3)
             assert torch.equal(out[b:b + 1], o1), f"same={same} sequence {b}"
             assert torch.equal(lse[b:b + 1], l1), f"same={same} sequence {b} lse"
+
+
+@pytest.mark.parametrize("D,w,kv_tied", [(256, 64, False), (256, 0, False), (512, 0, False), (512, 0, True)])
+def test_prefill_wide_kv_row_stride(gpu_lib, D, w, kv_tied):
+    """K and V (or X) read through views whose key-row stride is 2^20 elements (2 MiB): the byte offset
+    of key 2048 from key 0 is 2^32, past 32 bits, while each 32-key tile's offsets stay within them.
+    The output must be bit-identical to the same call on contiguous copies (the kernels' arithmetic
+    does not depend on where the rows are), which is itself checked against the oracle."""
+    g4 = gpu_lib
+    B, S, Hq, Hkv, W = 1, 2049, 2, 1, 1 << 20
+    q = _bf((B, S, Hq, D), 71)
+    kc, vc = _bf((B, S, Hkv, D), 72), _bf((B, S, Hkv, D), 73)
+    big = torch.empty((S, W), dtype=torch.bfloat16, device=DEV)          # 4 GiB + 2 MiB
+    big[:, :D] = kc[0, :, 0]
+    big[:, D:2 * D] = vc[0, :, 0]
+    strides = (S * W, W, D, 1)
+    kw = big.as_strided((B, S, Hkv, D), strides, 0)
+    vw = big.as_strided((B, S, Hkv, D), strides, D)
+    desc = g4.layer_desc(Hq, Hkv, D, window=w, k_eq_v=kv_tied, rotary_dims=128 if kv_tied else D)
+    wk = gen.norm_weight(D, (7, 66, 74, 0)).to(DEV) if kv_tied else None
+    out_w, out_c = torch.empty_like(q), torch.empty_like(q)
+    g4.g4attn_prefill(desc, q, kw, None if kv_tied else vw, out_w, w_k=wk)
+    g4.g4attn_prefill(desc, q, kc, None if kv_tied else vc, out_c, w_k=wk)
+    torch.cuda.synchronize()
+    del big
+    assert torch.equal(out_w, out_c), f"wide-stride rows differ D={D} w={w} K=V={kv_tied}"
+    if kv_tied:
+        K, V = onr.kv_tied_k_v(f64(kc), f64(wk), np.arange(S)[None, :], 128, desc.rope_theta)
+    else:
+        K, V = f64(kc), f64(vc)
+    ro, _ = oat.attention_band(f64(q), K, V, desc.scale, w)
+    assert_parity(f64(out_c), ro, f"wide-stride reference D={D} w={w} K=V={kv_tied}")
