@@ -17,7 +17,7 @@ Sources
   512 on E2B/E4B and 1024 on 31B/26B ["Window sizes by model family"].
 * Global layers: every earlier key is visible, and the layer stays causal
   [vinija.ai Gemma 4 primer, "Global attention layers"; Gemma 4 Keras docs,
-  "What changed from Gemma 3" (global layers stay causal)].
+  "What changed from Gemma 3" (causal masking kept on global layers)].
 * GQA: several query heads share one key/value head [Gemma 4 Keras docs,
   ``Gemma4Model`` table, ``num_kv_heads``; gemma4-pt-claude README,
   "Supported Models"].
