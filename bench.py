@@ -47,7 +47,7 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 # change, the roofline reports traffic as null until the counters are re-taken.
 PREFILL_TRAFFIC = {
     "sources": ["prefill.hip", "g4attn_internal.h", "norm_rope.hip", "abi.hip"],
-    "sources_sha256": "5a00d9a03b5e9e34e42ba160f2fbb1338b93be66004442aba86c61fabc6faa7c",
+    "sources_sha256": "a7dc3a0aa6be68bfddf5196bf443ca3a8c86b865b09a162dd1efada91ff7fbbf",
     "fetch_kib": 3.23965e6, "fetch_scale": 2.0,
     "write_kib": 1.28787e6, "write_scale": 1.0,
 }

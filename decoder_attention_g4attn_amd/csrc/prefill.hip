@@ -745,7 +745,8 @@ void prefill_d256_kernel(PrefillArgs a) {
       g = (int)((L / ntiles) % a.Hkv);
       b = (int)(L / ((int64_t)ntiles * a.Hkv));
     } else {
-      wg_map(ntiles, a.Hkv, b, g, tile, a.window > 0);
+      // sliding layers longer than their window: most tiles cost the same
+      wg_map(ntiles, a.Hkv, b, g, tile, a.window > 0 && a.S > a.window);
     }
 
     // Rows t < n of this sequence are positions P + t (P = 0, n = S unless
