@@ -244,3 +244,29 @@ def test_prefill_chunk_tied_validation():
     assert call(xc=MISALIGNED, ws=FAKE, wsb=1 << 30) == g4.ERR_LAYOUT
     # only the flags are needed: [1, 4, 1 tile, 4 waves] ints, 256-byte aligned
     assert call(ws=FAKE, wsb=255) == g4.ERR_WORKSPACE
+
+
+def test_binding_checks_tensors_before_calling_the_library():
+    """The binding refuses host tensors, wrong dtypes and wrong shapes itself (the C ABI sees only
+    pointers), before any library call."""
+    import torch
+    desc = _desc(head_dim=256, rotary_dims=256)
+    q = torch.zeros((1, 4, 32, 256), dtype=torch.bfloat16)
+    kv = torch.zeros((1, 4, 4, 256), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        g4.g4attn_prefill(desc, q, kv, kv, torch.empty_like(q))
+    with pytest.raises(TypeError):
+        g4.g4attn_prefill(desc, q.float(), kv, kv, q)
+
+    class Dev:  # a stand-in with the attributes the shape check reads
+        is_cuda = True
+
+        def __init__(self, shape, dtype=torch.bfloat16):
+            self.shape, self.dtype = shape, dtype
+
+    g4._expect(Dev((1, 4, 32, 256)), (1, 4, 32, 256), "q")
+    g4._expect(None, (1,), "optional")
+    with pytest.raises(ValueError, match="shape"):
+        g4._expect(Dev((1, 4, 16, 256)), (1, 4, 32, 256), "q")
+    with pytest.raises(TypeError):
+        g4._expect(Dev((2,), torch.int64), (2,), "pos0", torch.int32)
