@@ -53,18 +53,41 @@ PREFILL_TRAFFIC = {
 }
 
 
-def measured_traffic():
-    """Scaled HBM bytes per launch of the K=V prefill kernel, or None if its sources changed."""
+# MFMA counters of the prefill main kernels from one rocprofv3 pass each
+# (SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE; per
+# dispatch): counted flop = 512 x MOPS, busy = busy cycles / (1024 SIMDs x
+# GRBM_GUI_ACTIVE / 8), average clock = (GRBM_GUI_ACTIVE / 8) / duration.
+# The same source hash guards them.
+PREFILL_MFMA = {
+    "global": {"kernel": "prefill_kernel<512,K=V>", "counted_flop": 3.5219e13, "busy": 0.718,
+               "avg_clock_GHz": 1.64, "duration_ms_under_counters": 28.56},
+    "sliding": {"kernel": "prefill_d256_kernel", "counted_flop": 1.1317e12, "busy": 0.544,
+                "avg_clock_GHz": 1.91, "duration_ms_under_counters": 1.037},
+}
+
+
+def sources_unchanged():
+    """True while the kernel sources hash to the one the counters were taken on."""
     import hashlib
     csrc = os.path.join(ROOT, "decoder_attention_g4attn_amd", "csrc")
     h = hashlib.sha256()
     for f in PREFILL_TRAFFIC["sources"]:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
-    if h.hexdigest() != PREFILL_TRAFFIC["sources_sha256"]:
+    return h.hexdigest() == PREFILL_TRAFFIC["sources_sha256"]
+
+
+def measured_traffic():
+    """Scaled HBM bytes per launch of the K=V prefill kernel, or None if its sources changed."""
+    if not sources_unchanged():
         return None
     t = PREFILL_TRAFFIC
     return (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024.0
+
+
+def measured_mfma():
+    """Counted MFMA work, utilisation and clock of the prefill kernels, or None if their sources changed."""
+    return PREFILL_MFMA if sources_unchanged() else None
 
 
 def parse():
@@ -618,7 +641,8 @@ def main():
                 "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
                 "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
                 "kernel": "g4attn_prefill on the 31B K=V global layer (K=V pre-pass + prefill_kernel<512,K=V>)",
-                "flops_per_launch": fl_global}
+                "flops_per_launch": fl_global,
+                "mfma_counters": measured_mfma()}
     out = {
         "metric": "prefill attention TFLOP/s (31B global/sliding) + decode KV GB/s, 1xMI355X",
         "value": round(value, 3) if value else None,
