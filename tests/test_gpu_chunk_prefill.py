@@ -139,3 +139,45 @@ def test_prefill_chunk_padded_batch_equals_single_bit_exact(gpu_lib, D, w):
                                 torch.tensor([qlen[b]], dtype=torch.int32, device=DEV), 299, lse=l1)
         assert torch.equal(out[b:b + 1].view(torch.int16), o1.view(torch.int16)), f"sequence {b}"
         assert torch.equal(lse[b:b + 1, :, :qlen[b]], l1[:, :, :qlen[b]]), f"sequence {b} lse"
+
+
+def _random_chunk_configs(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        D = int(rng.choice([256, 512]))
+        Hkv = int(rng.choice([1, 2]))
+        G = int(rng.choice([1, 2, 8]))
+        w = int(rng.choice([0, 0, 1, 17, 64]))
+        B = int(rng.integers(1, 4))
+        total = [int(rng.integers(1, 300)) for _ in range(B)]
+        pos0 = [int(rng.integers(0, t)) for t in total]
+        # the chunk reaches the end of the cache, or stops short (its tail is then padding)
+        qlen = [t - p if rng.integers(0, 2) else int(rng.integers(1, t - p + 1)) for t, p in zip(total, pos0)]
+        out.append((B, G * Hkv, Hkv, D, w, tuple(total), tuple(pos0), tuple(qlen)))
+    return out
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,w,total,pos0,qlen", _random_chunk_configs(10, 11))
+def test_prefill_chunk_random_configs_vs_oracle(gpu_lib, B, Hq, Hkv, D, w, total, pos0, qlen):
+    """Seeded random chunks: offsets, chunk lengths (down to one row), padding, windows and head
+    groupings drawn together; padding rows stay untouched."""
+    g4 = gpu_lib
+    S = max(qlen)
+    cap = max(total) + 8
+    kc, vc = _caches(B, Hkv, cap, D, total, 500 + cap)
+    q = _bf((B, S, Hq, D), 600 + S)
+    out = torch.full((B, S, Hq, D), SENTINEL, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=DEV)
+    desc = g4.layer_desc(Hq, Hkv, D, window=w, rotary_dims=D)
+    g4.g4attn_prefill_chunk(desc, q, kc, vc, out, torch.tensor(pos0, dtype=torch.int32, device=DEV),
+                            torch.tensor(qlen, dtype=torch.int32, device=DEV),
+                            max(p + n - 1 for p, n in zip(pos0, qlen)), lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = oat.prefill_over_cache(f64(q), f64(kc), f64(vc), list(pos0), list(qlen), desc.scale, w)
+    got = np.concatenate([f64(out[b, :qlen[b]]).ravel() for b in range(B)])
+    ref = np.concatenate([ro[b, :qlen[b]].ravel() for b in range(B)])
+    assert_parity(got, ref, f"random chunk B={B} Hq={Hq} Hkv={Hkv} D={D} w={w} pos0={pos0} qlen={qlen}")
+    for b in range(B):
+        np.testing.assert_allclose(lse[b, :, :qlen[b]].cpu().numpy(), rl[b, :, :qlen[b]], rtol=0, atol=2e-3)
+        assert bool((out[b, qlen[b]:].view(torch.int16) == SENTINEL).all()), f"padding rows of sequence {b} written"

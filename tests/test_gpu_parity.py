@@ -427,3 +427,33 @@ def test_prefill_wide_kv_row_stride(gpu_lib, D, w, kv_tied):
         K, V = f64(kc), f64(vc)
     ro, _ = oat.attention_band(f64(q), K, V, desc.scale, w)
     assert_parity(f64(out_c), ro, f"wide-stride reference D={D} w={w} K=V={kv_tied}")
+
+
+# ------------------------------------------------------------------ randomized decode
+def _random_decode_configs(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        D = int(rng.choice([256, 512]))
+        Hkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.choice([1, 2, 4, 8, 16]))
+        B = int(rng.integers(1, 5))
+        # lengths: random, plus the edges (one row, exact tile and chunk multiples)
+        lens = [int(rng.choice([1, 16, 256, int(rng.integers(1, 1500))])) for _ in range(B)]
+        cap = max(lens) + int(rng.integers(0, 40))
+        same = bool(rng.integers(0, 2))
+        splits = int(rng.choice([0, 1, 3]))
+        out.append((B, G * Hkv, Hkv, D, tuple(lens), cap, same, splits))
+    return out
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,lens,cap,same,splits", _random_decode_configs(10, 7))
+def test_decode_random_configs_vs_oracle(gpu_lib, B, Hq, Hkv, D, lens, cap, same, splits):
+    """Seeded random decode shapes: batch, head grouping, width, lengths (with their edge values),
+    capacity, shared or separate caches and split count drawn together."""
+    g4 = gpu_lib
+    q, kc, vc, out, lse, desc = _decode_case(g4, B, Hq, Hkv, D, list(lens), cap, same, splits, seed=300 + cap)
+    kcn = f64(kc)
+    ro, rl = oat.decode_attention(f64(q), kcn, kcn if same else f64(vc), np.array(lens), desc.scale)
+    assert_parity(f64(out), ro, f"random decode B={B} Hq={Hq} Hkv={Hkv} D={D} lens={lens} same={same}")
+    np.testing.assert_allclose(lse.cpu().numpy(), rl, rtol=0, atol=2e-3)
