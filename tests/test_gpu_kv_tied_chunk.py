@@ -145,3 +145,44 @@ def test_prefill_tied_spans_vs_oracle(gpu_lib, Hq, Hkv):
         ro, rl = oat.attention_masked(f64(q[b:b + 1]), K[b:b + 1], V[b:b + 1], desc.scale, m)
         assert_parity(f64(out[b:b + 1]), ro, f"K=V spans b={b}")
         np.testing.assert_allclose(lse[b:b + 1].cpu().numpy(), rl, rtol=0, atol=1e-2)
+
+
+def _random_tied_chunk_configs(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        Hkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.choice([1, 4, 8]))
+        w = int(rng.choice([0, 0, 33, 128]))
+        B = int(rng.integers(1, 4))
+        total = [int(rng.integers(1, 260)) for _ in range(B)]
+        pos0 = [int(rng.integers(0, t)) for t in total]
+        qlen = [t - p if rng.integers(0, 2) else int(rng.integers(1, t - p + 1)) for t, p in zip(total, pos0)]
+        out.append((B, G * Hkv, Hkv, w, tuple(total), tuple(pos0), tuple(qlen)))
+    return out
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,w,total,pos0,qlen", _random_tied_chunk_configs(8, 13))
+def test_prefill_chunk_tied_random_configs(gpu_lib, B, Hq, Hkv, w, total, pos0, qlen):
+    """Seeded random K=V chunks over the raw-projection cache: offsets, chunk lengths (down to one
+    row), padding, windows and head groupings drawn together."""
+    g4 = gpu_lib
+    S, cap = max(qlen), max(total) + 8
+    X = _bf((B, max(total), Hkv, D), 40 + cap)
+    wk = gen.norm_weight(D, (7, 123, 41, 0)).to(DEV)
+    xc, rc, kc = _cache(g4, X, wk, cap)
+    q = _bf((B, S, Hq, D), 42 + S)
+    out = torch.full((B, S, Hq, D), SENTINEL, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=DEV)
+    desc = g4.layer_desc(Hq, Hkv, D, window=w, k_eq_v=True, rotary_dims=ROT, rope_theta=THETA)
+    g4.g4attn_prefill_chunk_tied(desc, q, xc, rc, kc, wk, out, torch.tensor(pos0, dtype=torch.int32, device=DEV),
+                                 torch.tensor(qlen, dtype=torch.int32, device=DEV), lse=lse)
+    torch.cuda.synchronize()
+    K, V = _oracle_kv(X, wk)
+    ro, rl = oat.prefill_over_cache(f64(q), K, V, list(pos0), list(qlen), desc.scale, w)
+    got = np.concatenate([f64(out[b, :qlen[b]]).ravel() for b in range(B)])
+    ref = np.concatenate([ro[b, :qlen[b]].ravel() for b in range(B)])
+    assert_parity(got, ref, f"random K=V chunk B={B} Hq={Hq} Hkv={Hkv} w={w} pos0={pos0} qlen={qlen}")
+    for b in range(B):
+        np.testing.assert_allclose(lse[b, :, :qlen[b]].cpu().numpy(), rl[b, :, :qlen[b]], rtol=0, atol=1e-2)
+        assert bool((out[b, qlen[b]:].view(torch.int16) == SENTINEL).all()), f"padding rows of sequence {b} written"
