@@ -32,6 +32,34 @@ def test_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+def test_header_serves_a_plain_c_caller(tmp_path):
+    """The header is plain C99 (no C++ types leak into the signatures) and a C program links
+    against the library and gets a host-side validation error back without any GPU."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "caller.c"
+    src.write_text(
+        "#include <stdio.h>\n#include \"g4attn.h\"\n"
+        "int main(void) {\n"
+        "  g4attn_status s = g4attn_prefill(NULL, NULL, NULL, NULL, NULL, NULL, NULL, 1, 1, NULL, NULL, NULL,\n"
+        "                                   NULL, NULL, NULL, 0, NULL);\n"
+        "  printf(\"%d %d %s\\n\", (int)g4attn_version(), (int)s, g4attn_status_str(s));\n"
+        "  return s == G4ATTN_ERR_NULL ? 0 : 1;\n}\n")
+    exe = tmp_path / "caller"
+    libdir = os.path.dirname(g4.LIB_PATH)
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.dirname(HEADER),
+                        str(src), "-o", str(exe), "-L", libdir, "-lg4attn", f"-Wl,-rpath,{libdir}"],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    version, status, text = r.stdout.split(" ", 2)
+    assert int(version) == g4.load().g4attn_version() and int(status) == 1 and "NULL" in text
+
+
 def test_version_and_status_strings():
     assert g4.g4attn_version() == 400
     for s in range(8):
