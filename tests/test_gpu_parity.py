@@ -95,6 +95,40 @@ def test_norm_rope_positions_and_cache_mode(gpu_lib):
     del written
 
 
+@pytest.mark.parametrize("D,H", [(256, 1), (256, 5), (256, 12), (256, 33), (512, 1), (512, 3), (512, 6), (512, 9)])
+def test_norm_rope_head_groups(gpu_lib, D, H):
+    """Head counts that leave the last wave of a token with fewer heads than it holds."""
+    g4 = gpu_lib
+    B, S = 2, 9
+    rot, theta = (D, 1e4) if D == 256 else (128, 1e6)
+    wide = _bf((B, S, 2 * H, D), 70 + H, 2.0)
+    x = wide[:, :, ::2]                      # strided heads
+    w = _w(D, 71)
+    y = torch.empty_like(x)
+    g4.g4attn_norm_rope(x, y, w, D, rot, theta)
+    y_contig = torch.empty_like(x)
+    g4.g4attn_norm_rope(x.contiguous(), y_contig, w, D, rot, theta)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_contig)
+    pos = np.tile(np.arange(S), (B, 1))
+    ref = onr.norm_rope(f64(x), f64(w), pos, rot, theta)
+    ulp = np.maximum(np.abs(ref), 1e-30) * 2.0 ** -7
+    assert np.all(np.abs(f64(y) - ref) <= ulp + 1e-5)
+    # cache mode: rows pos0[b] + t of [B, H, cap, D]; nothing else written
+    cap = 40
+    pos0 = torch.tensor([3, 20], dtype=torch.int32, device=DEV)
+    cache = torch.full((B, H, cap, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    g4.g4attn_norm_rope(x, cache, w, D, rot, theta, pos0=pos0, cache_cap=cap)
+    y_pos = torch.empty_like(x)
+    g4.g4attn_norm_rope(x, y_pos, w, D, rot, theta, pos0=pos0)
+    torch.cuda.synchronize()
+    for b, p0 in enumerate(pos0.tolist()):
+        assert torch.equal(cache[b, :, p0:p0 + S].permute(1, 0, 2), y_pos[b])
+        keep = torch.ones(cap, dtype=torch.bool)
+        keep[p0:p0 + S] = False
+        assert torch.isnan(cache[b][:, keep].float()).all()
+
+
 # ------------------------------------------------------------------ prefill
 PREFILL_CASES = [
     # B, S, Hq, Hkv, D, window
@@ -183,7 +217,8 @@ def test_prefill_poisoned_tails(gpu_lib):
     assert torch.equal(out, ref)
 
 
-@pytest.mark.parametrize("B,S,Hq,Hkv", [(1, 1, 8, 1), (1, 40, 8, 1), (1, 300, 32, 4), (2, 129, 16, 2)])
+@pytest.mark.parametrize("B,S,Hq,Hkv", [(1, 1, 8, 1), (1, 40, 8, 1), (1, 300, 32, 4), (2, 129, 16, 2),
+                                     (1, 70, 15, 5), (2, 33, 6, 3)])
 def test_prefill_kv_tied_vs_oracle(gpu_lib, B, S, Hq, Hkv):
     g4 = gpu_lib
     D, rot, theta = 512, 128, 1e6
