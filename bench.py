@@ -100,6 +100,8 @@ def parse():
                                        "e2b_sliding", "e2b_global", "kvchunk"],
                     default=None,
                     help="time one stage only (profiling aid)")
+    ap.add_argument("--attainable", action="store_true",
+                    help="run only the attainable-rate measurements (roofline probes, copy, GEMM) and print them")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device-to-device copy 3 times (HBM-counter calibration)")
     return ap.parse_args()
@@ -120,8 +122,13 @@ def copy_calibration():
 
 def attainable(torch):
     """Measured attainable rates on this GPU, as context for the roofline
-    fractions: a plain device copy of 2 GiB (read + write bytes over time)
-    and a large bf16 GEMM through torch (the vendor library's MFMA path)."""
+    fractions: the two roofline probes of libg4probe.so (a bare bf16 MFMA
+    loop, one workgroup of 4 waves per CU for ~30 ms like the K=V prefill,
+    on random operands like the attention's data and again on operands that
+    barely switch, which let the chip hold its clock; and an 8 GiB non-temporal
+    streaming read), a plain device copy of 2 GiB
+    (read + write bytes over time) and a large bf16 GEMM through torch (the
+    vendor library's MFMA path)."""
     def timed(fn, reps):
         fn()
         torch.cuda.synchronize()
@@ -143,7 +150,27 @@ def attainable(torch):
     b = torch.randn(m, m, device="cuda").to(torch.bfloat16)
     ms = timed(lambda: torch.matmul(a, b), 5)
     gemm = 2.0 * m ** 3 / ms / 1e9
-    return {"hbm_copy_GBps": round(copy_gbps, 1), "bf16_gemm_8192_tflops": round(gemm, 1)}
+    del a, b
+    from decoder_attention_g4attn_amd import probe
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(cus * 256, dtype=torch.float32, device="cuda")
+    iters = 1 << 18
+    flop = float(cus) * 4 * iters * 8 * 32768
+    ms = timed(lambda: probe.mfma_bf16(out, cus, iters, probe.RANDOM), 3)
+    mfma = flop / ms / 1e9
+    ms = timed(lambda: probe.mfma_bf16(out, cus, iters, probe.LOW_ACTIVITY), 3)
+    mfma_low = flop / ms / 1e9
+    del out
+    src = torch.empty(8 << 30, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    wgs = 2 * cus
+    sink = torch.empty(wgs * 256, dtype=torch.int32, device="cuda")
+    ms = timed(lambda: probe.stream_read(src, sink, wgs), 5)
+    rd = float(src.numel()) / ms / 1e6
+    del src, sink
+    return {"mfma_loop_bf16_tflops": round(mfma, 1), "mfma_loop_bf16_low_activity_tflops": round(mfma_low, 1),
+            "stream_read_GBps": round(rd, 1),
+            "hbm_copy_GBps": round(copy_gbps, 1), "bf16_gemm_8192_tflops": round(gemm, 1)}
 
 
 class Stage:
@@ -516,6 +543,10 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    if args.attainable:
+        import torch
+        print(json.dumps(attainable(torch)))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the attention path shards by KV head / batch without collectives).", file=sys.stderr)
@@ -678,8 +709,12 @@ def main():
         "roofline": roof,
     }
     if args.only is None:
-        log("measuring attainable copy and GEMM rates")
+        log("measuring attainable rates: MFMA loop, streaming read, copy, GEMM")
         att = attainable(torch)
+        att["global_prefill_frac_of_mfma_loop"] = round(res["global_prefill_tflops"] / att["mfma_loop_bf16_tflops"], 4)
+        att["sliding_prefill_frac_of_mfma_loop"] = round(res["sliding_prefill_tflops"] / att["mfma_loop_bf16_tflops"],
+                                                         4)
+        att["decode_frac_of_stream_read"] = round(res["decode_GBps"] / att["stream_read_GBps"], 4)
         att["global_prefill_frac_of_gemm"] = round(res["global_prefill_tflops"] / att["bf16_gemm_8192_tflops"], 4)
         att["decode_frac_of_copy"] = round(res["decode_GBps"] / att["hbm_copy_GBps"], 4)
         out["attainable"] = att

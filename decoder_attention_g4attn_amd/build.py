@@ -1,9 +1,11 @@
-"""Build libg4attn.so in-tree with hipcc for gfx950.
+"""Build libg4attn.so and libg4probe.so in-tree with hipcc for gfx950.
 
     python -m decoder_attention_g4attn_amd.build [-v]
 
 Every HIP source under csrc/ is compiled to an object in _build/ and linked
-into ``decoder_attention_g4attn_amd/libg4attn.so``.  Always recompiles.
+into ``decoder_attention_g4attn_amd/libg4attn.so``; the roofline probes under
+probes/ go into ``decoder_attention_g4attn_amd/libg4probe.so``.  Always
+recompiles.
 """
 
 import concurrent.futures as cf
@@ -17,6 +19,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libg4attn.so")
+PROBES = os.path.join(PKG, "probes")
+PROBE_LIB = os.path.join(PKG, "libg4probe.so")
 ARCH = "gfx950"
 
 CXXFLAGS = [
@@ -57,18 +61,25 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose=False):
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=4) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), sources()))
-    tmp = LIB + ".tmp"
+def _link(objs, lib, verbose):
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print("built", LIB)
+        print("built", lib)
+
+
+def build(verbose=False):
+    os.makedirs(BUILD, exist_ok=True)
+    probe_srcs = sorted(os.path.join(PROBES, f) for f in os.listdir(PROBES) if f.endswith(".hip"))
+    with cf.ThreadPoolExecutor(max_workers=4) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), sources() + probe_srcs))
+    n = len(objs) - len(probe_srcs)
+    _link(objs[:n], LIB, verbose)
+    _link(objs[n:], PROBE_LIB, verbose)
     return LIB
 
 
