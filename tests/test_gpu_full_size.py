@@ -17,61 +17,11 @@ from g4inputs import WORKLOADS, gen
 from oracle import norm_rope as onr
 
 from tests._cmp import assert_parity
+from tests._rows import LSE_ATOL, prefill_oracle_rows, sample_tokens
 
 pytestmark = pytest.mark.gpu
 
 f64 = gen.to_f64
-
-# The prologue hands q and k to attention as bf16 (half-ulp 2^-9 relative),
-# while the oracle keeps them in fp64, so each logit scale * q.k moves by up
-# to about 2^-8 |scale q.k|: 0.01 for the largest logits here (about 2.5 in
-# magnitude for RMS-normalised rows with N(1, 0.1) weights and random
-# directions, up to ~4 in the tails).  The log-sum-exp is a weighted mean of
-# the logits' errors, so it gets the same bound.
-LSE_ATOL = 1e-2
-
-
-def _sample_tokens(S, window, n_rand, seed):
-    """First/last tokens, 32-key tile edges, window edges and seeded random positions."""
-    fixed = {0, 1, 31, 32, 33, 127, 128, S // 2, S - 2, S - 1}
-    if window:
-        fixed |= {window - 1, window, window + 1, min(S - 1, 2 * window + 5)}
-    rng = np.random.default_rng(seed)
-    rand = set(rng.integers(0, S, size=n_rand).tolist())
-    return np.array(sorted(t for t in fixed | rand if 0 <= t < S), dtype=np.int64)
-
-
-def _prefill_oracle_rows(s, b, g, toks, heads):
-    """Oracle out [len(toks), len(heads), D] and lse for batch b, KV group g."""
-    c = s["c"]
-    slo, shi = gen.image_spans(c.S, c.images)
-    hi = int(max(toks.max(), shi[toks].max())) + 1
-    lo = 0 if c.window == 0 else max(0, int(min(toks.min() - c.window + 1, slo[toks].min())))
-    pos_k = np.arange(lo, hi)[None, :]
-    if c.k_eq_v:
-        X = f64(s["X"][b:b + 1, lo:hi, g:g + 1])
-        K, V = onr.kv_tied_k_v(X, f64(s["wk"]), pos_k, c.rotary_dims, c.theta)
-    else:
-        K = onr.norm_rope(f64(s["k_raw"][b:b + 1, lo:hi, g:g + 1]), f64(s["wk"]), pos_k, c.rotary_dims, c.theta)
-        V = onr.norm_rope(f64(s["v_raw"][b:b + 1, lo:hi, g:g + 1]), None, pos_k, 0, c.theta)
-    out = np.zeros((len(toks), len(heads), c.D))
-    lse = np.zeros((len(toks), len(heads)))
-    for ti, t in enumerate(toks):
-        qraw = f64(s["q_raw"][b:b + 1, t:t + 1, heads])                 # [1, 1, H, D]
-        q = onr.norm_rope(qraw, f64(s["wq"]), np.array([[t]]), c.rotary_dims, c.theta)
-        k0 = 0 if c.window == 0 else max(0, int(t) - c.window + 1)
-        # visible keys of row t: its window (or every earlier key), plus its image block
-        keys = sorted(set(range(k0, int(t) + 1)) | set(range(int(slo[t]), int(shi[t]) + 1)))
-        kk = K[0, np.asarray(keys) - lo, 0]
-        vv = V[0, np.asarray(keys) - lo, 0]
-        for hi_, _ in enumerate(heads):
-            sc = c.scale * (kk @ q[0, 0, hi_])
-            m = sc.max()
-            e = np.exp(sc - m)
-            out[ti, hi_] = (e @ vv) / e.sum()
-            lse[ti, hi_] = m + np.log(e.sum())
-    return out, lse
-
 
 @pytest.mark.parametrize("name", ["e2b_sliding_prefill", "e2b_global_prefill", "31b_sliding_prefill",
                                   "31b_global_kv_prefill", "31b_sliding_image_prefill"])
@@ -86,12 +36,12 @@ def test_full_size_prefill_sampled_rows(gpu_lib, name):
     got_all, ref_all = [], []
     for b in range(c.B):
         for g in range(c.Hkv):
-            toks = _sample_tokens(c.S, c.window, n_rand=6 if c.Hkv > 4 else 12, seed=(c.cfg_id, b, g))
+            toks = sample_tokens(c.S, c.window, n_rand=6 if c.Hkv > 4 else 12, seed=(c.cfg_id, b, g))
             for st, n in c.images[:3]:      # rows at and inside image blocks
                 toks = np.union1d(toks, [st, st + n // 2, st + n - 1])
             # two query heads of the group: the first and the last
             heads = sorted({g * G, g * G + G - 1})
-            ro, rl = _prefill_oracle_rows(s, b, g, toks, heads)
+            ro, rl = prefill_oracle_rows(s, b, g, toks, heads)
             ti = torch.as_tensor(toks, device="cuda")
             hi = torch.as_tensor(heads, device="cuda")
             got = f64(s["out"][b].index_select(0, ti).index_select(1, hi))
@@ -156,7 +106,7 @@ def test_full_size_chunk_prefill_sampled_rows(gpu_lib):
     got_all, ref_all = [], []
     for b in range(c.B):
         for g in (0, 7, 15):
-            toks = _sample_tokens(c.S, 0, n_rand=6, seed=(c.cfg_id, b, g))
+            toks = sample_tokens(c.S, 0, n_rand=6, seed=(c.cfg_id, b, g))
             heads = [g * G, g * G + G - 1]
             for t in toks:
                 p = s["p0"] + int(t)
@@ -192,7 +142,7 @@ def test_full_size_kv_chunk_prefill_sampled_rows(gpu_lib):
         K, V = onr.kv_tied_k_v(f64(X[0:1, :, g:g + 1]), f64(s["wk"]), np.arange(s["total"])[None, :],
                                c.rotary_dims, c.theta)
         kk, vv = K[0, :, 0], V[0, :, 0]
-        toks = _sample_tokens(c.S, 0, n_rand=6, seed=(c.cfg_id, 0, g))
+        toks = sample_tokens(c.S, 0, n_rand=6, seed=(c.cfg_id, 0, g))
         heads = [g * G, g * G + G - 1]
         for t in toks:
             p = s["p0"] + int(t)
