@@ -104,11 +104,12 @@ __global__ __launch_bounds__(256) void norm_rope_kernel(NormRopeArgs a) {
   // of branching; only heads below H are stored).  Loads complete in issue
   // order, so the small weight loads go first: waiting for them must not
   // wait for the rows as well.
-  // Without a weight the loads read the first row instead and the factors
-  // are replaced by 1 after they arrive (a branch around the loads would
-  // wait for them inside it).
+  // Without a weight the loads read the wave's own first row instead (never
+  // one another wave writes in place) and the factors are replaced by 1
+  // after they arrive (a branch around the loads would wait for them inside
+  // it).
   float c[E], s[E], wl[E], wh[E];
-  const uint16_t* wsrc = a.w ? a.w : a.x + b * a.xs[0] + t * a.xs[1];
+  const uint16_t* wsrc = a.w ? a.w : a.x + b * a.xs[0] + t * a.xs[1] + h0 * a.xs[2];
   Vec<E>::load(wsrc + j0, wl);
   Vec<E>::load(wsrc + HALF + j0, wh);
   float lo[HB][E], hi[HB][E];

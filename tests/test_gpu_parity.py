@@ -129,6 +129,24 @@ def test_norm_rope_head_groups(gpu_lib, D, H):
         assert torch.isnan(cache[b][:, keep].float()).all()
 
 
+@pytest.mark.parametrize("D,H", [(256, 12), (512, 9), (256, 1)])
+@pytest.mark.parametrize("weighted", [True, False])
+def test_norm_rope_in_place_equals_out_of_place(gpu_lib, D, H, weighted):
+    """x == y (equal strides) is allowed: several waves per token then write
+    rows of one token while others read theirs."""
+    g4 = gpu_lib
+    B, S = 2, 33
+    rot, theta = (D, 1e4) if D == 256 else (128, 1e6)
+    x = _bf((B, S, H, D), 80 + H, 2.0)
+    w = _w(D, 81) if weighted else None
+    y = torch.empty_like(x)
+    g4.g4attn_norm_rope(x, y, w, D, rot, theta)
+    z = x.clone()
+    g4.g4attn_norm_rope(z, z, w, D, rot, theta)
+    torch.cuda.synchronize()
+    assert torch.equal(z, y)
+
+
 # ------------------------------------------------------------------ prefill
 PREFILL_CASES = [
     # B, S, Hq, Hkv, D, window
