@@ -96,10 +96,11 @@ WORKLOADS = {
 }
 
 
-# Parity cases at the longest context the pages give the 31B model (256K
-# positions: "Gemma 4" Keras docs and the vinija.ai primer, context windows
-# by variant).  Shapes of the 31B layers above at S = 262144; not timed by the
-# bench (they exist to exercise 64-bit offsets and full-length index logic).
+# Parity cases at the longest contexts the pages give (256K positions on the
+# 31B model, 128K on E2B: "Gemma 4" Keras docs and the vinija.ai primer,
+# context windows by variant).  Shapes of the layers above at those lengths;
+# not timed by the bench (they exist to exercise 64-bit offsets and
+# full-length index logic).
 MAX_CONTEXT = {
     "31b_global_kv_prefill_256k": Workload(
         "31b_global_kv_prefill_256k", 11, "prefill", B=1, S=262144, Hq=32, Hkv=4, D=512,
@@ -107,6 +108,12 @@ MAX_CONTEXT = {
     "31b_sliding_prefill_256k": Workload(
         "31b_sliding_prefill_256k", 12, "prefill", B=1, S=262144, Hq=32, Hkv=16, D=256,
         window=1024, rotary_dims=256, theta=1e4, k_eq_v=False),
+    "e2b_global_prefill_128k": Workload(
+        "e2b_global_prefill_128k", 14, "prefill", B=1, S=131072, Hq=8, Hkv=1, D=512,
+        window=0, rotary_dims=128, theta=1e6, k_eq_v=False),
+    "e2b_sliding_prefill_128k": Workload(
+        "e2b_sliding_prefill_128k", 15, "prefill", B=1, S=131072, Hq=8, Hkv=1, D=256,
+        window=512, rotary_dims=256, theta=1e4, k_eq_v=False),
     # two sequences whose new token is the 262144th position
     "31b_global_kv_decode_256k": Workload(
         "31b_global_kv_decode_256k", 13, "decode", B=2, S=1, Hq=32, Hkv=4, D=512,

@@ -1,11 +1,12 @@
-"""Parity at the longest context the pages give: 256K positions on the 31B
-model ("Gemma 4" Keras docs and the vinija.ai Gemma 4 primer, context windows
-by variant).
+"""Parity at the longest contexts the pages give: 256K positions on the 31B
+model, 128K on E2B ("Gemma 4" Keras docs and the vinija.ai Gemma 4 primer,
+context windows by variant).
 
 At S = 262144 the 31B global layer's q holds exactly 2^32 elements, so these
 cases exercise every 64-bit offset of the prologue, prefill and decode
 kernels, and the index logic over the whole length:
-- the K=V global and the sliding prefill, run as the bench runs its
+- the 31B K=V global and sliding prefills at 256K and the E2B global
+  (separate K and V) and sliding prefills at 128K, run as the bench runs its
   workloads (prologue + attention), with sampled rows (tile edges deep in
   the sequence included) against the fp64 oracle, then with a logit scale of
   0, where rint(exp(lse)) must equal the visible-key count of every row and
@@ -66,23 +67,25 @@ def _zero_scale(g4, c):
                          rope_theta=c.theta, scale=0.0)
 
 
-@pytest.mark.parametrize("name", ["31b_global_kv_prefill_256k", "31b_sliding_prefill_256k"])
-def test_prefill_256k_sampled_rows_and_counts(gpu_lib, name):
+@pytest.mark.parametrize("name", ["31b_global_kv_prefill_256k", "31b_sliding_prefill_256k",
+                                  "e2b_global_prefill_128k", "e2b_sliding_prefill_128k"])
+def test_prefill_max_context_sampled_rows_and_counts(gpu_lib, name):
     g4 = gpu_lib
     c = MAX_CONTEXT[name]
-    print(f"[256k] {name}: inputs and run", flush=True)
+    print(f"[max] {name}: inputs and run", flush=True)
     s = bench.build_prefill(torch, g4, gen, c)
     lse = torch.empty((c.B, c.Hq, c.S), dtype=torch.float32, device="cuda")
     bench.run_prefill(g4, s, lse=lse)
     torch.cuda.synchronize()
     assert torch.isfinite(lse).all()
     G = c.Hq // c.Hkv
-    deep = [32767, 32768, 131071, 131072, 262111, 262112]     # 32-key tile edges far into the sequence
+    # 32-key tile edges far into the sequence
+    deep = [t for t in (32767, 32768, 65535, 65536, 131071, 131072, 262111, 262112) if t < c.S]
     got_all, ref_all = [], []
-    for g in (0, c.Hkv - 1):
+    for g in sorted({0, c.Hkv - 1}):
         toks = np.union1d(sample_tokens(c.S, c.window, n_rand=4, seed=(c.cfg_id, 0, g)), deep)
         heads = sorted({g * G, g * G + G - 1})
-        print(f"[256k] {name}: oracle rows of KV group {g}", flush=True)
+        print(f"[max] {name}: oracle rows of KV group {g}", flush=True)
         ro, rl = prefill_oracle_rows(s, 0, g, toks, heads)
         ti = torch.as_tensor(toks, device="cuda")
         hi = torch.as_tensor(heads, device="cuda")
@@ -93,7 +96,7 @@ def test_prefill_256k_sampled_rows_and_counts(gpu_lib, name):
     assert_parity(np.concatenate([x.reshape(-1) for x in got_all]),
                   np.concatenate([x.reshape(-1) for x in ref_all]), f"{name} sampled rows")
 
-    print(f"[256k] {name}: counts", flush=True)
+    print(f"[max] {name}: counts", flush=True)
     s["desc"] = _zero_scale(g4, c)
     bench.run_prefill(g4, s, lse=lse)
     torch.cuda.synchronize()
