@@ -104,6 +104,33 @@ __device__ __forceinline__ void load_rows(const uint16_t* base, int row0, int nr
 // recomputed by the REDO launch with the true maxima (every P <= 1 then).
 constexpr float kHeadroom = 64.f;
 
+// A chunk's normalised O and log-sum-exp.  With one chunk per (sequence,
+// KV head) they are the result itself (the combine of a single partial has
+// weight exp(0) = 1 and returns the same bits), so the split kernel writes
+// out and lse directly and the combine launch is skipped.
+template <int D>
+__device__ __forceinline__ void write_chunk(const DecodeArgs& a, int64_t ph, int split, int d, float o, float lse) {
+  if (a.nsplit == 1) {
+    a.out[ph * D + d] = (uint16_t)f2bf(o);
+    if (d == 0 && a.lse) a.lse[ph] = lse;
+  } else {
+    a.o_part[(ph * a.nsplit + split) * D + d] = o;
+    if (d == 0) a.lse_part[ph * a.nsplit + split] = lse;
+  }
+}
+
+// A sequence with no rows (kv_len clamped to 0) and one chunk: nothing else
+// writes its heads, so the split kernel writes what the combine would (zeros,
+// lse = -inf).
+template <int D>
+__device__ void write_empty(const DecodeArgs& a, int b, int g, int G, int nthreads) {
+  for (int idx = threadIdx.x; idx < G * D; idx += nthreads) {
+    const int64_t ph = (int64_t)b * a.Hq + g * G + idx / D;
+    a.out[ph * D + idx % D] = 0;
+    if (idx % D == 0 && a.lse) a.lse[ph] = -INFINITY;
+  }
+}
+
 template <int D, bool SAME_KV, bool REDO>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   typedef DCfg<D, SAME_KV> C;
@@ -132,6 +159,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const int n = min(max(a.kv_len[b], 0), a.max_len);
   const int r0 = split * a.chunk;
   if (r0 >= n) {  // beyond this sequence: the combine never reads it
+    if (!REDO && a.nsplit == 1) write_empty<D>(a, b, g, G, C::WAVES * 64);
     if (!REDO) return;
     continue;
   }
@@ -274,8 +302,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       O += wt * so[(w * 16 + hh) * D + d];
     }
     const int64_t ph = (int64_t)b * a.Hq + g * G + hh;
-    a.o_part[(ph * a.nsplit + split) * D + d] = O / L;
-    if (d == 0) a.lse_part[ph * a.nsplit + split] = (M + __log2f(L)) * kLn2;
+    write_chunk<D>(a, ph, split, d, O / L, (M + __log2f(L)) * kLn2);
   }
   if (!REDO) return;
   __syncthreads();  // every wave is done with the LDS before the next chunk reuses it
@@ -328,6 +355,7 @@ __global__ __launch_bounds__(kWavesT * 64) void decode_tied_kernel(DecodeArgs a)
   const int n = min(max(a.kv_len[b], 0), a.max_len);
   const int r0 = split * a.chunk;
   if (r0 >= n) {  // beyond this sequence: the combine never reads it
+    if (!REDO && a.nsplit == 1) write_empty<D>(a, b, g, G, kWavesT * 64);
     if (!REDO) return;
     continue;
   }
@@ -484,8 +512,7 @@ __global__ __launch_bounds__(kWavesT * 64) void decode_tied_kernel(DecodeArgs a)
       O += wt * so[(w * 16 + hh) * D + d];
     }
     const int64_t ph = (int64_t)b * a.Hq + g * G + hh;
-    a.o_part[(ph * a.nsplit + split) * D + d] = O / L;
-    if (d == 0) a.lse_part[ph * a.nsplit + split] = (M + __log2f(L)) * kLn2;
+    write_chunk<D>(a, ph, split, d, O / L, (M + __log2f(L)) * kLn2);
   }
   if (!REDO) return;
   __syncthreads();  // every wave is done with the LDS before the next chunk reuses it
@@ -532,7 +559,7 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_split_kernel<D, SAME, true>), redo_grid(grid), dim3(C::WAVES * 64), 0, st, a);
   e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || a.nsplit == 1) return e;  // one chunk: the split kernel wrote the result
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.Hq, a.B), dim3(256), 0, st, a);
   return hipGetLastError();
 }
@@ -546,7 +573,7 @@ hipError_t launch_decode_tied(const DecodeArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_tied_kernel<true>, redo_grid(grid), dim3(kWavesT * 64), 0, st, a);
   e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || a.nsplit == 1) return e;  // one chunk: the split kernel wrote the result
   hipLaunchKernelGGL((decode_combine_kernel<512>), dim3(a.Hq, a.B), dim3(256), 0, st, a);
   return hipGetLastError();
 }

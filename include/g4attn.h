@@ -275,6 +275,9 @@ size_t g4attn_decode_workspace_bytes(const g4attn_layer_desc* desc, int32_t B,
  *   v_cache    same shape; may equal k_cache (one tensor serves as both).
  *   kv_len     device int32 [B]; each value in [1, max_kv_len]: the number of
  *              positions of the sequence so far, the new token included.
+ *              The kernels clamp it to [0, max_kv_len], so no row past
+ *              max_kv_len is read; a sequence clamped to 0 gets zeros and
+ *              lse = -inf.
  *              Global layer (window == 0): rows [0, kv_len[b]) are read,
  *              rows past them never.  Sliding layer (window > 0): k_cache and
  *              v_cache are rings of cache_cap == window slots (position p in
@@ -293,7 +296,8 @@ size_t g4attn_decode_workspace_bytes(const g4attn_layer_desc* desc, int32_t B,
  *              64 rows each), with
  *              rows = max_kv_len (global) or min(max_kv_len, window)
  *              (sliding); the partial results are merged by a log-sum-exp
- *              combine.
+ *              combine (with one chunk per sequence the split kernel writes
+ *              the result itself and no combine runs).
  *   workspace  >= g4attn_decode_workspace_bytes(desc, B, max_kv_len,
  *              num_splits) bytes, 16-byte aligned.
  */

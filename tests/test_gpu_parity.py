@@ -288,6 +288,29 @@ def test_decode_vs_oracle(gpu_lib, D, same, splits):
     assert torch.equal(out[0], vc[0, :, 0].repeat_interleave(G, dim=0))
 
 
+@pytest.mark.parametrize("D,splits", [(256, 1), (512, 1), (512, 3)])
+def test_decode_clamped_lengths(gpu_lib, D, splits):
+    """kv_len is clamped to [0, max_kv_len] on the device: a length of 0 (or
+    below) gives zeros and lse = -inf, one past max_kv_len reads only
+    max_kv_len rows; the other sequences are unaffected."""
+    g4 = gpu_lib
+    B, Hq, Hkv, cap, maxlen = 4, 8, 2, 200, 150
+    lens = [0, 37, -5, maxlen + 9]
+    q, kc, vc, out, lse, desc = _decode_case(g4, B, Hq, Hkv, D, [1, 37, 1, maxlen], cap, False, splits)
+    kv_len = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    out.fill_(1.0)
+    g4.g4attn_decode(desc, q, kc, vc, kv_len, maxlen, out, lse=lse, num_splits=splits)
+    torch.cuda.synchronize()
+    for b in (0, 2):
+        assert torch.count_nonzero(out[b]) == 0
+        assert torch.isneginf(lse[b]).all()
+    for b, n in ((1, 37), (3, maxlen)):
+        ro, rl = oat.decode_attention(f64(q[b:b + 1]), f64(kc[b:b + 1, :, :n]), f64(vc[b:b + 1, :, :n]), [n],
+                                      desc.scale)
+        assert_parity(f64(out[b:b + 1]), ro, f"clamped decode b={b}")
+        np.testing.assert_allclose(lse[b:b + 1].cpu().numpy(), rl, rtol=0, atol=2e-3)
+
+
 def test_decode_split_counts_agree_and_shared_cache(gpu_lib):
     g4 = gpu_lib
     lens = [2000, 4097, 33]
