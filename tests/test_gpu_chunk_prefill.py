@@ -158,7 +158,7 @@ def _random_chunk_configs(n, seed):
     return out
 
 
-@pytest.mark.parametrize("B,Hq,Hkv,D,w,total,pos0,qlen", _random_chunk_configs(10, 11))
+@pytest.mark.parametrize("B,Hq,Hkv,D,w,total,pos0,qlen", _random_chunk_configs(20, 11))
 def test_prefill_chunk_random_configs_vs_oracle(gpu_lib, B, Hq, Hkv, D, w, total, pos0, qlen):
     """Seeded random chunks: offsets, chunk lengths (down to one row), padding, windows and head
     groupings drawn together; padding rows stay untouched."""

@@ -162,7 +162,7 @@ def _random_tied_chunk_configs(n, seed):
     return out
 
 
-@pytest.mark.parametrize("B,Hq,Hkv,w,total,pos0,qlen", _random_tied_chunk_configs(8, 13))
+@pytest.mark.parametrize("B,Hq,Hkv,w,total,pos0,qlen", _random_tied_chunk_configs(20, 13))
 def test_prefill_chunk_tied_random_configs(gpu_lib, B, Hq, Hkv, w, total, pos0, qlen):
     """Seeded random K=V chunks over the raw-projection cache: offsets, chunk lengths (down to one
     row), padding, windows and head groupings drawn together."""

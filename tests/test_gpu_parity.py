@@ -417,7 +417,7 @@ def _random_configs(n, seed):
     return out
 
 
-@pytest.mark.parametrize("B,S,Hq,Hkv,D,w", _random_configs(12, 2024))
+@pytest.mark.parametrize("B,S,Hq,Hkv,D,w", _random_configs(30, 2024))
 def test_prefill_random_configs_vs_oracle(gpu_lib, B, S, Hq, Hkv, D, w):
     """Seeded random shapes: lengths, windows, head groupings and widths drawn together."""
     g4 = gpu_lib
@@ -523,7 +523,7 @@ def _random_decode_configs(n, seed):
     return out
 
 
-@pytest.mark.parametrize("B,Hq,Hkv,D,lens,cap,same,splits", _random_decode_configs(10, 7))
+@pytest.mark.parametrize("B,Hq,Hkv,D,lens,cap,same,splits", _random_decode_configs(25, 7))
 def test_decode_random_configs_vs_oracle(gpu_lib, B, Hq, Hkv, D, lens, cap, same, splits):
     """Seeded random decode shapes: batch, head grouping, width, lengths (with their edge values),
     capacity, shared or separate caches and split count drawn together."""
