@@ -40,7 +40,7 @@ def _oracle_kv(X, wk):
     return K.transpose(0, 2, 1, 3), V.transpose(0, 2, 1, 3)
 
 
-@pytest.mark.parametrize("Hq,Hkv,w", [(8, 1, 0), (16, 2, 0), (8, 2, 100)])
+@pytest.mark.parametrize("Hq,Hkv,w", [(8, 1, 0), (16, 2, 0), (8, 2, 100), (16, 1, 0)])
 def test_prefill_chunk_tied_vs_oracle(gpu_lib, Hq, Hkv, w):
     g4 = gpu_lib
     total = [300, 150, 97]          # positions each sequence holds so far, this chunk's included

@@ -49,7 +49,7 @@ def test_kv_tied_append_rows(gpu_lib):
     assert bool(torch.isnan(xc[0, :, S:]).all()) and bool(torch.isnan(rc[1, :, :55]).all())
 
 
-@pytest.mark.parametrize("Hq,Hkv,splits", [(32, 4, 0), (8, 1, 3), (16, 2, 1)])
+@pytest.mark.parametrize("Hq,Hkv,splits", [(32, 4, 0), (8, 1, 3), (16, 2, 1), (16, 1, 0), (16, 1, 2)])
 def test_decode_tied_vs_oracle(gpu_lib, Hq, Hkv, splits):
     g4 = gpu_lib
     lens = [1, 17, 300, 1029, 64]

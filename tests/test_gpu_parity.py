@@ -154,6 +154,8 @@ PREFILL_CASES = [
     (2, 65, 4, 2, 256, 64), (1, 129, 8, 1, 256, 512), (1, 300, 2, 2, 256, 100), (1, 700, 8, 1, 256, 512),
     (1, 1, 8, 1, 512, 0), (1, 17, 8, 1, 512, 0), (2, 130, 4, 1, 512, 0), (1, 257, 8, 2, 512, 0),
     (1, 200, 32, 4, 512, 0), (1, 99, 32, 16, 256, 32), (1, 50, 3, 1, 256, 0), (1, 45, 6, 2, 512, 7),
+    # 12B global layer (16 query heads on one KV head), E4B sliding layer (4 per KV head, window 512)
+    (1, 90, 16, 1, 512, 0), (1, 70, 16, 1, 256, 33), (1, 150, 8, 2, 256, 512),
 ]
 
 
@@ -236,7 +238,7 @@ def test_prefill_poisoned_tails(gpu_lib):
 
 
 @pytest.mark.parametrize("B,S,Hq,Hkv", [(1, 1, 8, 1), (1, 40, 8, 1), (1, 300, 32, 4), (2, 129, 16, 2),
-                                     (1, 70, 15, 5), (2, 33, 6, 3)])
+                                     (1, 70, 15, 5), (2, 33, 6, 3), (1, 200, 16, 1), (2, 45, 16, 1)])
 def test_prefill_kv_tied_vs_oracle(gpu_lib, B, S, Hq, Hkv):
     g4 = gpu_lib
     D, rot, theta = 512, 128, 1e6
