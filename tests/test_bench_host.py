@@ -59,3 +59,14 @@ def test_cpu_baseline_runs_on_small_stand_ins(monkeypatch):
     assert set(out["per_config"]) == {"e2b_sliding_prefill", "e2b_global_prefill", "31b_sliding_prefill",
                                       "31b_global_kv_prefill", "31b_global_kv_decode"}
     assert all(v["value"] > 0 and v["sample"] for v in out["per_config"].values())
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """One GPU only: --gpus N > 1 exits non-zero with a message, before touching a GPU."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], cwd=root,
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0 and "one GPU" in r.stderr
