@@ -114,6 +114,13 @@ MAX_CONTEXT = {
     "e2b_sliding_prefill_128k": Workload(
         "e2b_sliding_prefill_128k", 15, "prefill", B=1, S=131072, Hq=8, Hkv=1, D=256,
         window=512, rotary_dims=256, theta=1e4, k_eq_v=False),
+    # chunked prefills of the last 4096 of 262144 positions over the caches
+    "31b_global_kv_chunk_256k": Workload(
+        "31b_global_kv_chunk_256k", 16, "chunk", B=1, S=4096, Hq=32, Hkv=4, D=512,
+        window=0, rotary_dims=128, theta=1e6, k_eq_v=True, len_lo=262144, len_hi=262144),
+    "31b_sliding_chunk_256k": Workload(
+        "31b_sliding_chunk_256k", 17, "chunk", B=1, S=4096, Hq=32, Hkv=16, D=256,
+        window=1024, rotary_dims=256, theta=1e4, k_eq_v=False, len_lo=262144, len_hi=262144),
     # two sequences whose new token is the 262144th position
     "31b_global_kv_decode_256k": Workload(
         "31b_global_kv_decode_256k", 13, "decode", B=2, S=1, Hq=32, Hkv=4, D=512,

@@ -11,6 +11,9 @@ kernels, and the index logic over the whole length:
   the sequence included) against the fp64 oracle, then with a logit scale of
   0, where rint(exp(lse)) must equal the visible-key count of every row and
   head exactly wherever fp32 can carry it (see EXACT_COUNT);
+- the K=V and sliding chunked prefills of the last 4096 of 262144 positions
+  over their caches (raw projection for K=V, linear K/V for sliding), sampled
+  rows and counts as above;
 - the K=V decode of two sequences whose new token is the 262144th position,
   sampled heads against the oracle, then the same counts at three split
   counts.
@@ -103,6 +106,68 @@ def test_prefill_max_context_sampled_rows_and_counts(gpu_lib, name):
     expect = _expected_counts(c.S, c.window, np.union1d(deep, [0, 1, 1023, 1024, 1025, c.S - 1]))
     got = _counts(lse)
     exact = expect <= EXACT_COUNT
+    rel = np.abs(np.exp(lse[0].cpu().numpy().astype(np.float64)) / expect[None, :] - 1.0)
+    for h in range(c.Hq):
+        np.testing.assert_array_equal(got[0, h][exact], expect[exact], err_msg=f"{name} counts h={h}")
+    assert np.all(rel[:, ~exact] <= 4 * 2.0 ** -23 * 12.5), f"{name} counts past 2^17: {rel[:, ~exact].max()}"
+
+
+@pytest.mark.parametrize("name", ["31b_global_kv_chunk_256k", "31b_sliding_chunk_256k"])
+def test_chunk_256k_sampled_rows_and_counts(gpu_lib, name):
+    g4 = gpu_lib
+    c = MAX_CONTEXT[name]
+    print(f"[max] {name}: inputs and run", flush=True)
+    s = (bench.build_kv_chunk if c.k_eq_v else bench.build_chunk)(torch, g4, gen, c)
+    lse = torch.empty((c.B, c.Hq, c.S), dtype=torch.float32, device="cuda")
+
+    def run(desc):
+        bench.run_chunk_pro(g4, s)
+        if c.k_eq_v:
+            g4.g4attn_prefill_chunk_tied(desc, s["q"], s["xc"], s["rc"], s["krc"], s["wk"], s["out"], s["pos0"],
+                                         s["qlen"], s["total"] - 1, lse=lse, workspace=s["ws"])
+        else:
+            g4.g4attn_prefill_chunk(desc, s["q"], s["kc"], s["vc"], s["out"], s["pos0"], s["qlen"],
+                                    s["total"] - 1, lse=lse, workspace=s["ws"])
+        torch.cuda.synchronize()
+
+    run(s["desc"])
+    G = c.Hq // c.Hkv
+    p0, total = s["p0"], s["total"]
+    got_all, ref_all = [], []
+    for g in (0, c.Hkv - 1):
+        print(f"[max] {name}: oracle rows of KV group {g}", flush=True)
+        if c.k_eq_v:   # the oracle's keys and values from the raw rows the cache was built from
+            X = gen.normal_bf16((c.B, total, c.Hkv, c.D), gen.seed_key(c.cfg_id, gen.X), "cuda")
+            K, V = onr.kv_tied_k_v(f64(X[0:1, :, g:g + 1]), f64(s["wk"]), np.arange(total)[None, :],
+                                   c.rotary_dims, c.theta)
+            del X
+            kk_all, vv_all = K[0, :, 0], V[0, :, 0]
+        toks = sample_tokens(c.S, 0, n_rand=4, seed=(c.cfg_id, 0, g))
+        heads = [g * G, g * G + G - 1]
+        for t in toks:
+            p = p0 + int(t)
+            k0 = 0 if c.window == 0 else p - c.window + 1
+            if c.k_eq_v:
+                kk, vv = kk_all[k0:p + 1], vv_all[k0:p + 1]
+            else:
+                kk, vv = f64(s["kc"][0, g, k0:p + 1]), f64(s["vc"][0, g, k0:p + 1])
+            q = onr.norm_rope(f64(s["q_raw"][0:1, t:t + 1, heads]), f64(s["wq"]), np.array([[p]]), c.rotary_dims,
+                              c.theta)
+            for hi_, h in enumerate(heads):
+                sc = c.scale * (kk @ q[0, 0, hi_])
+                m = sc.max()
+                e = np.exp(sc - m)
+                ref_all.append((e @ vv) / e.sum())
+                got_all.append(f64(s["out"][0, t, h]))
+                np.testing.assert_allclose(float(lse[0, h, t]), m + np.log(e.sum()), rtol=0, atol=LSE_ATOL,
+                                           err_msg=f"{name} t={t} h={h} lse")
+    assert_parity(np.stack(got_all), np.stack(ref_all), f"{name} sampled rows")
+
+    print(f"[max] {name}: counts", flush=True)
+    run(_zero_scale(g4, c))
+    expect = _expected_counts(total, c.window, [p0, p0 + 1, total - 1])[p0:total]
+    exact = expect <= EXACT_COUNT
+    got = _counts(lse)
     rel = np.abs(np.exp(lse[0].cpu().numpy().astype(np.float64)) / expect[None, :] - 1.0)
     for h in range(c.Hq):
         np.testing.assert_array_equal(got[0, h][exact], expect[exact], err_msg=f"{name} counts h={h}")
