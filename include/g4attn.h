@@ -290,8 +290,8 @@ size_t g4attn_decode_workspace_bytes(const g4attn_layer_desc* desc, int32_t B,
  *              is G4ATTN_ERR_SHAPE.
  *   out        [B, Hq, D] bf16 contiguous;  lse  [B, Hq] fp32 or NULL.
  *   num_splits 0 = automatic (about one workgroup per compute unit over
- *              B * Hkv (sequence, KV head) pairs: ceil(256 / (B * Hkv))
- *              chunks of at least 256 rows); otherwise the row range
+ *              B * Hkv (sequence, KV head) pairs: min(32, ceil(256 / (B *
+ *              Hkv))) chunks of at least 256 rows); otherwise the row range
  *              [0, rows) is cut into num_splits equal chunks (a multiple of
  *              64 rows each), with
  *              rows = max_kv_len (global) or min(max_kv_len, window)
