@@ -887,6 +887,19 @@ void prefill_d256_kernel(PrefillArgs a) {
       if (kt_lo < kt_hi) load_tile_w(lds0 + C::STAGE, kt_lo + 1);
     }
 
+    // The workgroup walks the band of all its rows; a tile holding no key
+    // that any of this wave's rows sees adds exact zeros to O and l, so the
+    // wave skips its MFMAs and softmax (it still copies and meets the
+    // barrier) and the other wave on its SIMD gets the matrix core.  Spans
+    // widen the visible set, so with spans every tile is computed.
+    const int64_t Fw0 = F0 + wave * 32;
+    const int pw0 = P + (int)(Fw0 / G);
+    const int pw1 = P + min((int)((Fw0 + 31) / G), n - 1);
+    auto wave_sees = [&](int kt) {
+      const int key0 = kt * kBN;
+      return spans || (pw0 <= pw1 && key0 <= pw1 && (a.window == 0 || key0 + kBN - 1 > pw0 - a.window));
+    };
+
     f32x16 oacc[C::NC];
 #pragma unroll
     for (int c = 0; c < C::NC; ++c) oacc[c] = f32x16{};
@@ -899,6 +912,10 @@ void prefill_d256_kernel(PrefillArgs a) {
         wait_vmem_all();
       __syncthreads();  // all of tile kt is in LDS; every wave is done with tile kt-1
       if (kt > kt_lo && kt < kt_hi) load_tile_w(lds0 + (C::STAGE - so), kt + 1);
+      if (!wave_sees(kt)) {
+        so = C::STAGE - so;
+        continue;
+      }
       f32x16 s = qk(so);
       if (!REDO && __builtin_amdgcn_ballot_w64(m_ref == -INFINITY)) {
         const float rowmx = max_xor32(tile_max(s, kt));
