@@ -47,9 +47,9 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 # change, the roofline reports traffic as null until the counters are re-taken.
 PREFILL_TRAFFIC = {
     "sources": ["prefill.hip", "g4attn_internal.h", "norm_rope.hip", "abi.hip"],
-    "sources_sha256": "ae42325219442d7c2eacfc2c7890ac190723e56ddc2a9f7a71d1eebc2f18127c",
-    "fetch_kib": 3.23946e6, "fetch_scale": 2.0,
-    "write_kib": 1.30643e6, "write_scale": 1.0,
+    "sources_sha256": "dafcd3beb9b2e2e28e5634e334f40b9f4126815df21d7066560dad7991deaf3a",
+    "fetch_kib": 3.23950e6, "fetch_scale": 2.0,
+    "write_kib": 1.31073e6, "write_scale": 1.0,
 }
 
 
@@ -59,10 +59,10 @@ PREFILL_TRAFFIC = {
 # GRBM_GUI_ACTIVE / 8), average clock = (GRBM_GUI_ACTIVE / 8) / duration.
 # The same source hash guards them.
 PREFILL_MFMA = {
-    "global": {"kernel": "prefill_kernel<512,K=V>", "counted_flop": 3.5219e13, "busy": 0.708,
-               "avg_clock_GHz": 1.66, "duration_ms_under_counters": 28.65},
-    "sliding": {"kernel": "prefill_d256_kernel", "counted_flop": 1.1317e12, "busy": 0.548,
-                "avg_clock_GHz": 1.87, "duration_ms_under_counters": 1.054},
+    "global": {"kernel": "prefill_kernel<512,K=V>", "counted_flop": 3.5219e13, "busy": 0.710,
+               "avg_clock_GHz": 1.62, "duration_ms_under_counters": 29.24},
+    "sliding": {"kernel": "prefill_d256_kernel", "counted_flop": 1.0984e12, "busy": 0.522,
+                "avg_clock_GHz": 1.87, "duration_ms_under_counters": 1.077},
 }
 
 
